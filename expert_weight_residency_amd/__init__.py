@@ -1,0 +1,208 @@
+"""Hot/cold expert-residency MXFP4 MoE layer for MI355X (gfx950).
+
+A thin ctypes binding over ``libmoe_residency.so``: every function here has the
+name of a C entry point in ``include/moe_residency.h`` and only marshals
+arguments (torch tensors -> device pointers, the current HIP stream). Every
+step of the layer runs in the library's HIP kernels; there is no fallback, and
+importing a function whose library is missing raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_residency.so")
+
+MOE_OK, MOE_EINVAL, MOE_EHIP, MOE_ESTALE, MOE_ENOTSUP = 0, -1, -2, -3, -4
+MOE_MAX_EXPERTS = MOE_MAX_ROWS = 4096
+MOE_MAX_TOPK = 32
+
+# entry points declared in include/moe_residency.h
+ENTRY_POINTS = ("moe_expert_bytes", "moe_ffn_workspace_bytes", "moe_route_split",
+                "moe_expert_ffn_mxfp4", "moe_finalize", "moe_usage_counts", "moe_swap_rows",
+                "moe_last_error")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class MoeStale(MoeError):
+    """moe_swap_rows refused a swap decided against outdated owner lists."""
+
+
+class MoeBankC(ctypes.Structure):
+    _fields_ = [("w13", ctypes.c_void_p), ("s13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("s2", ctypes.c_void_p), ("n_rows", ctypes.c_int32), ("on_host", ctypes.c_int32)]
+
+
+class MoeSplitC(ctypes.Structure):
+    _fields_ = [("n_active", ctypes.c_void_p), ("active_rows", ctypes.c_void_p),
+                ("row_off", ctypes.c_void_p), ("slots", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} (run `make lib` or "
+                               "__graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.moe_expert_bytes.restype = sz
+        L.moe_expert_bytes.argtypes = [i32, i32]
+        L.moe_ffn_workspace_bytes.restype = sz
+        L.moe_ffn_workspace_bytes.argtypes = [i32, i32, i32]
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_route_split.restype = i32
+        L.moe_route_split.argtypes = [vp, i32, i32, vp, i32, i32, i32, vp, i32, MoeSplitC,
+                                      MoeSplitC, vp, vp]
+        L.moe_expert_ffn_mxfp4.restype = i32
+        L.moe_expert_ffn_mxfp4.argtypes = [ctypes.POINTER(MoeBankC), MoeSplitC, vp, i32, i32, i32,
+                                           i32, vp, vp, vp]
+        L.moe_finalize.restype = i32
+        L.moe_finalize.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+        L.moe_usage_counts.restype = i32
+        L.moe_usage_counts.argtypes = [vp, i32, i32, vp, vp]
+        L.moe_swap_rows.restype = i32
+        L.moe_swap_rows.argtypes = [ctypes.POINTER(MoeBankC), ctypes.POINTER(MoeBankC), i32, i32,
+                                    i32, i32, vp, i32, vp, vp, vp, sz, i32, i32, vp]
+        _lib = L
+    return _lib
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != MOE_OK:
+        msg = moe_last_error()
+        raise (MoeStale if rc == MOE_ESTALE else MoeError)(rc, msg)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def moe_expert_bytes(H: int, I: int) -> int:
+    return int(lib().moe_expert_bytes(H, I))
+
+
+def moe_ffn_workspace_bytes(T: int, k: int, I: int) -> int:
+    return int(lib().moe_ffn_workspace_bytes(T, k, I))
+
+
+# ------------------------------------------------------------ containers --
+
+@dataclass
+class Bank:
+    """One residency bank: uint8 tensors w13 [R,2I,H/2], s13 [R,2I,H/32],
+    w2 [R,H,I/2], s2 [R,H,I/32] on the device, or pinned on the host
+    (on_host=True, read in place by the kernels)."""
+    w13: object
+    s13: object
+    w2: object
+    s2: object
+    on_host: bool = False
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.w13.shape[0])
+
+    def abi(self) -> MoeBankC:
+        return MoeBankC(self.w13.data_ptr(), self.s13.data_ptr(), self.w2.data_ptr(),
+                        self.s2.data_ptr(), self.n_rows, 1 if self.on_host else 0)
+
+    def tensors(self) -> dict:
+        return {"w13": self.w13, "s13": self.s13, "w2": self.w2, "s2": self.s2}
+
+
+@dataclass
+class Split:
+    """Device int32 buffers of one bank's split (see moe_split)."""
+    n_active: object
+    active_rows: object
+    row_off: object
+    slots: object
+
+    @classmethod
+    def empty(cls, n_rows: int, T: int, k: int, device="cuda") -> "Split":
+        import torch
+        cap = min(n_rows, T * k)
+        return cls(torch.zeros(1, dtype=torch.int32, device=device),
+                   torch.zeros(max(cap, 1), dtype=torch.int32, device=device),
+                   torch.zeros(cap + 1, dtype=torch.int32, device=device),
+                   torch.zeros(max(T * k, 1), dtype=torch.int32, device=device))
+
+    def abi(self) -> MoeSplitC:
+        return MoeSplitC(self.n_active.data_ptr(), self.active_rows.data_ptr(),
+                         self.row_off.data_ptr(), self.slots.data_ptr())
+
+    def to_host(self):
+        """(active_rows, row_off, slots) as numpy, trimmed to n_active."""
+        n = int(self.n_active.item())
+        off = self.row_off[: n + 1].cpu().numpy()
+        return (self.active_rows[:n].cpu().numpy(), off, self.slots[: int(off[-1])].cpu().numpy())
+
+
+# ---------------------------------------------------------- entry points --
+
+def moe_route_split(topk_ids, row_map, n_hot_rows: int, n_cold_rows: int, hot: Split, cold: Split,
+                    n_invalid, counts_layer=None, count_tmax: int = 256, stream=None) -> None:
+    T, k = int(topk_ids.shape[0]), int(topk_ids.shape[1])
+    _check(lib().moe_route_split(_ptr(topk_ids), T, k, row_map.data_ptr(), int(row_map.shape[0]),
+                                 n_hot_rows, n_cold_rows, _ptr(counts_layer), count_tmax,
+                                 hot.abi(), cold.abi(), n_invalid.data_ptr(), _stream(stream)))
+
+
+def moe_expert_ffn_mxfp4(bank: Bank, split: Split, x, k: int, I: int, workspace, Y,
+                         stream=None) -> None:
+    T, H = int(x.shape[0]), int(x.shape[1])
+    b = bank.abi()
+    _check(lib().moe_expert_ffn_mxfp4(ctypes.byref(b), split.abi(), x.data_ptr(), T, k, H, I,
+                                      workspace.data_ptr(), Y.data_ptr(), _stream(stream)))
+
+
+def moe_finalize(Y, topk_w, out, stream=None) -> None:
+    T, k = int(topk_w.shape[0]), int(topk_w.shape[1])
+    H = int(out.shape[1])
+    _check(lib().moe_finalize(Y.data_ptr(), topk_w.data_ptr(), T, k, H, out.data_ptr(),
+                              _stream(stream)))
+
+
+def moe_usage_counts(counts, host_dst, stream=None) -> None:
+    L, E = int(counts.shape[0]), int(counts.shape[1])
+    _check(lib().moe_usage_counts(counts.data_ptr(), L, E, host_dst.data_ptr(), _stream(stream)))
+
+
+def moe_swap_rows(hot: Bank, cold: Bank, hot_row: int, cold_row: int, expect_hot_expert: int,
+                  expect_cold_expert: int, row_map, hot_owner, cold_owner, staging, H: int, I: int,
+                  stream=None) -> None:
+    """hot_owner / cold_owner: host int32 arrays (numpy or CPU torch), updated in place."""
+    hb, cb = hot.abi(), cold.abi()
+
+    def hptr(a):
+        return a.ctypes.data if hasattr(a, "ctypes") else a.data_ptr()
+
+    nbytes = staging.numel() * staging.element_size()
+    _check(lib().moe_swap_rows(ctypes.byref(hb), ctypes.byref(cb), hot_row, cold_row,
+                               expect_hot_expert, expect_cold_expert, row_map.data_ptr(),
+                               int(row_map.shape[0]), hptr(hot_owner), hptr(cold_owner),
+                               staging.data_ptr(), nbytes, H, I, _stream(stream)))

@@ -1,0 +1,45 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_residency.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16 bits, round to nearest even; NaN keeps its sign and is quieted.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Launchers (each returns hipSuccess or the launch error). Arguments are
+// validated by the ABI layer before any of these runs.
+hipError_t launch_route_split(const int32_t* ids, int T, int k, const int32_t* row_map, int E,
+                              int n_hot, int n_cold, int32_t* counts, int count_on,
+                              const moe_split& hot, const moe_split& cold, int32_t* n_invalid,
+                              hipStream_t stream);
+
+hipError_t launch_ffn(const uint8_t* w13, const uint8_t* s13, const uint8_t* w2,
+                      const uint8_t* s2, int cap, const moe_split& split, const uint16_t* x, int T,
+                      int k, int H, int I, uint16_t* h_ws, uint16_t* Y, hipStream_t stream);
+
+hipError_t launch_finalize(const uint16_t* Y, const float* w, int T, int k, int H, uint16_t* out,
+                           hipStream_t stream);
+
+hipError_t launch_map_write(int32_t* row_map, int e_a, int v_a, int e_b, int v_b,
+                            hipStream_t stream);
+
+// Largest pick count handled by the single-kernel split.
+constexpr int kSplitSingleMaxPicks = 2048;
+
+}  // namespace moe

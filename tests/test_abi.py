@@ -1,0 +1,110 @@
+"""The C ABI library without a GPU: it loads, exports every function the
+header declares, and its host-side checks reject bad arguments before any
+GPU call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import expert_weight_residency_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_residency.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail(f"library not built: {moe.LIB_PATH}")
+    return moe.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(moe.ENTRY_POINTS), names
+    raw = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_sizes(L):
+    assert moe.moe_expert_bytes(4096, 2880) == 18_800_640
+    assert moe.moe_expert_bytes(256, 128) == 52_224
+    assert moe.moe_ffn_workspace_bytes(16, 6, 2880) == 16 * 6 * 2880 * 2
+    assert moe.moe_ffn_workspace_bytes(0, 6, 2880) == 0
+
+
+def _split(p=0x1000):
+    return moe.MoeSplitC(p, p, p, p)
+
+
+def test_route_split_rejects_bad_shapes(L):
+    p = 0x1000
+    assert L.moe_route_split(p, -1, 6, p, 384, 295, 89, None, 256, _split(), _split(), p, None) == moe.MOE_EINVAL
+    assert L.moe_route_split(p, 4, 0, p, 384, 295, 89, None, 256, _split(), _split(), p, None) == moe.MOE_EINVAL
+    assert L.moe_route_split(p, 4, 6, p, 0, 0, 0, None, 256, _split(), _split(), p, None) == moe.MOE_EINVAL
+    assert L.moe_route_split(p, 4, 6, p, 384, 5000, 89, None, 256, _split(), _split(), p, None) == moe.MOE_EINVAL
+    assert L.moe_route_split(p, 4, 6, None, 384, 295, 89, None, 256, _split(), _split(), p, None) == moe.MOE_EINVAL
+    assert L.moe_route_split(p, 4, 6, p, 384, 295, 89, None, 256, _split(0), _split(), p, None) == moe.MOE_EINVAL
+    assert "split" in moe.moe_last_error()
+
+
+def test_ffn_rejects_bad_shapes(L):
+    p = 0x1000
+    bank = moe.MoeBankC(p, p, p, p, 4, 0)
+    for (H, I) in ((4000, 2880), (4096, 2850), (0, 64)):
+        assert L.moe_expert_ffn_mxfp4(ctypes.byref(bank), _split(), p, 4, 2, H, I, p, p, None) == moe.MOE_EINVAL
+    assert L.moe_expert_ffn_mxfp4(None, _split(), p, 4, 2, 256, 128, p, p, None) == moe.MOE_EINVAL
+    # misaligned activations
+    assert L.moe_expert_ffn_mxfp4(ctypes.byref(bank), _split(), p + 2, 4, 2, 256, 128, p, p, None) == moe.MOE_EINVAL
+    # nothing to do is success without touching the GPU
+    empty = moe.MoeBankC(p, p, p, p, 0, 0)
+    assert L.moe_expert_ffn_mxfp4(ctypes.byref(empty), _split(), p, 4, 2, 256, 128, p, p, None) == moe.MOE_OK
+    assert L.moe_expert_ffn_mxfp4(ctypes.byref(bank), _split(), p, 0, 2, 256, 128, p, p, None) == moe.MOE_OK
+
+
+def test_finalize_and_counts_reject_bad_args(L):
+    p = 0x1000
+    assert L.moe_finalize(p, p, 4, 2, 12, p, None) == moe.MOE_EINVAL
+    assert L.moe_finalize(p, p, 4, 99, 16, p, None) == moe.MOE_EINVAL
+    assert L.moe_finalize(p, p, 0, 2, 16, p, None) == moe.MOE_OK
+    assert L.moe_usage_counts(p, 40, 0, p, None) == moe.MOE_EINVAL
+    assert L.moe_usage_counts(None, 40, 384, p, None) == moe.MOE_EINVAL
+
+
+def test_swap_stale_check_runs_on_host(L):
+    """A swap decided against outdated owner lists is refused before anything
+    is enqueued, and the mirrors are untouched."""
+    p = 0x1000
+    hot = moe.MoeBankC(p, p, p, p, 3, 0)
+    cold = moe.MoeBankC(p, p, p, p, 2, 0)
+    hot_owner = np.array([4, 5, 6], np.int32)
+    cold_owner = np.array([1, 2], np.int32)
+    need = moe.moe_expert_bytes(256, 128)
+    rc = L.moe_swap_rows(ctypes.byref(hot), ctypes.byref(cold), 1, 0, 6, 1, p, 8,
+                         hot_owner.ctypes.data, cold_owner.ctypes.data, p, need, 256, 128, None)
+    assert rc == moe.MOE_ESTALE
+    assert "stale" in moe.moe_last_error()
+    assert hot_owner.tolist() == [4, 5, 6] and cold_owner.tolist() == [1, 2]
+    # staging too small / bad rows are argument errors
+    assert L.moe_swap_rows(ctypes.byref(hot), ctypes.byref(cold), 1, 0, 5, 1, p, 8,
+                           hot_owner.ctypes.data, cold_owner.ctypes.data, p, need - 1, 256, 128,
+                           None) == moe.MOE_EINVAL
+    assert L.moe_swap_rows(ctypes.byref(hot), ctypes.byref(cold), 3, 0, 5, 1, p, 8,
+                           hot_owner.ctypes.data, cold_owner.ctypes.data, p, need, 256, 128,
+                           None) == moe.MOE_EINVAL
+
+
+def test_python_errors_raise(L):
+    with pytest.raises(moe.MoeError):
+        moe._check(moe.MOE_EINVAL)
+    with pytest.raises(moe.MoeStale):
+        moe._check(moe.MOE_ESTALE)

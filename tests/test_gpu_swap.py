@@ -1,0 +1,117 @@
+"""GPU row swaps at the pages' dry-run geometry (384 experts, 295 hot / 89
+cold; small expert shapes so the test is quick): five ordered swaps leave the
+layer output bit-identical and every expert's bytes where the map says; a map
+flip without the copies diverges; a stale swap is refused with nothing
+enqueued; a long swap sequence undone in reverse restores the banks byte for
+byte. Every step is mirrored on host byte arrays by the oracle's swap."""
+import numpy as np
+import pytest
+import torch
+
+import expert_weight_residency_amd as moe
+import oracle
+import synth
+from gpu_util import device_bank, host_bank, pinned_bank, run_layer
+
+pytestmark = pytest.mark.gpu
+
+E, N_COLD, K, H, I, SEED = 384, 89, 6, 256, 128, 77
+
+
+def _setup(cold_pinned=True):
+    rm, ho, co = synth.fitted_map(E, N_COLD, SEED, 0)
+    hot_h, cold_h = host_bank(ho, SEED, 0, H, I), host_bank(co, SEED, 0, H, I)
+    hot = device_bank(hot_h)
+    cold = pinned_bank(cold_h) if cold_pinned else device_bank(cold_h)
+    ob_hot, ob_cold = oracle.Bank(**{k: v.copy() for k, v in hot_h.items()}), \
+        oracle.Bank(**{k: v.copy() for k, v in cold_h.items()})
+    rm_dev = torch.from_numpy(rm.copy()).cuda()
+    staging = torch.empty(moe.moe_expert_bytes(H, I), dtype=torch.uint8, device="cuda")
+    return rm, ho.copy(), co.copy(), hot, cold, ob_hot, ob_cold, rm_dev, staging
+
+
+def _bank_equals(gbank, obank):
+    return all(np.array_equal(getattr(gbank, t).cpu().numpy(), getattr(obank, t))
+               for t in synth.TENSORS)
+
+
+def _layer(hot, cold, rm_np, ids, w, x):
+    return run_layer(hot, cold, rm_np, ids, w, x, H, I)[1]
+
+
+@pytest.mark.parametrize("cold_pinned", [True, False], ids=["cold_pinned", "cold_device"])
+def test_five_ordered_swaps(cold_pinned):
+    rm, ho, co, hot, cold, ob_hot, ob_cold, rm_dev, staging = _setup(cold_pinned)
+    rng = np.random.default_rng(1)
+    pairs = [(int(rng.integers(len(ho))), int(rng.integers(len(co)))) for _ in range(5)]
+    ids, w = synth.skewed_routing(16, K, E, SEED, 0, 0)
+    for n, (a, b) in enumerate(pairs):          # the swapped experts are routed to
+        ids[n, 0], ids[n, 1] = ho[a], co[b]
+    x = synth.activations(16, H, SEED)
+    out0 = _layer(hot, cold, rm, ids, w, x)
+    rm_host = rm.copy()
+    for n, (a, b) in enumerate(pairs):
+        e_h, e_c = int(ho[a]), int(co[b])
+        moe.moe_swap_rows(hot, cold, a, b, e_h, e_c, rm_dev, ho, co, staging, H, I)
+        oracle.swap_rows(ob_hot, ob_cold, a, b, e_h, e_c, rm_host, *_mirrors(ho, co, a, b, e_h, e_c))
+        torch.cuda.synchronize()
+        assert np.array_equal(rm_dev.cpu().numpy(), rm_host), n
+        assert _bank_equals(hot, ob_hot) and _bank_equals(cold, ob_cold), n
+        assert ho[a] == e_c and co[b] == e_h
+        out = _layer(hot, cold, rm_dev.cpu().numpy(), ids, w, x)
+        assert np.array_equal(out, out0), n
+
+
+def _mirrors(ho, co, a, b, e_h, e_c):
+    """The oracle swap checks and updates its own owner mirrors; give it copies
+    holding the pre-swap owners (the ABI call already updated ho / co)."""
+    oh, oc = ho.copy(), co.copy()
+    oh[a], oc[b] = e_h, e_c
+    return oh, oc
+
+
+def test_misordered_flip_diverges():
+    rm, ho, co, hot, cold, _, _, rm_dev, _ = _setup()
+    ids, w = synth.skewed_routing(16, K, E, SEED, 0, 1)
+    ids[0, 0], ids[1, 0] = ho[3], co[2]
+    x = synth.activations(16, H, SEED, step=1)
+    out0 = _layer(hot, cold, rm, ids, w, x)
+    bad = rm.copy()
+    bad[ho[3]], bad[co[2]] = -1 - 2, 3          # flip the map, skip the copies
+    out1 = _layer(hot, cold, bad, ids, w, x)
+    assert not np.array_equal(out0, out1)
+
+
+def test_stale_swap_refused_nothing_enqueued():
+    rm, ho, co, hot, cold, ob_hot, ob_cold, rm_dev, staging = _setup()
+    ho_before, co_before = ho.copy(), co.copy()
+    with pytest.raises(moe.MoeStale):
+        moe.moe_swap_rows(hot, cold, 4, 7, int(ho[5]), int(co[7]), rm_dev, ho, co, staging, H, I)
+    torch.cuda.synchronize()
+    assert np.array_equal(ho, ho_before) and np.array_equal(co, co_before)
+    assert np.array_equal(rm_dev.cpu().numpy(), rm)
+    assert _bank_equals(hot, ob_hot) and _bank_equals(cold, ob_cold)
+
+
+def test_swap_round_trip_restores_banks():
+    rm, ho, co, hot, cold, ob_hot, ob_cold, rm_dev, staging = _setup()
+    rng = np.random.default_rng(2)
+    log = []
+    for _ in range(60):
+        a, b = int(rng.integers(len(ho))), int(rng.integers(len(co)))
+        log.append((a, b, int(ho[a]), int(co[b])))
+        moe.moe_swap_rows(hot, cold, a, b, int(ho[a]), int(co[b]), rm_dev, ho, co, staging, H, I)
+    for a, b, e_h, e_c in reversed(log):
+        moe.moe_swap_rows(hot, cold, a, b, e_c, e_h, rm_dev, ho, co, staging, H, I)
+    torch.cuda.synchronize()
+    assert np.array_equal(rm_dev.cpu().numpy(), rm)
+    assert _bank_equals(hot, ob_hot) and _bank_equals(cold, ob_cold)
+
+
+def test_usage_counts_snapshot():
+    table = torch.arange(40 * E, dtype=torch.int32, device="cuda").reshape(40, E)
+    dst = torch.empty((40, E), dtype=torch.int32, pin_memory=True)
+    moe.moe_usage_counts(table, dst)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.numpy(), table.cpu().numpy())
+    assert dst.numel() * 4 == 61_440
