@@ -1,0 +1,372 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot/cold-residency MoE layer on one MI355X.
+
+Workload (default): one full-shape routed MoE layer per step -- 384 experts,
+top-6, hidden 4096, intermediate 2880 (one MXFP4 expert = 18,800,640 B), 16
+decode tokens, 295 hot expert rows in HBM and 89 cold rows in pinned host
+memory read in place, a residency map fitted to the routing distribution
+(about 1.7% of picks cold), skewed synthetic routing shaped after the pages'
+decode histogram. Steps rotate through --layers distinct layer banks and use
+fresh routing and activations each step, so the 256 MB Infinity Cache cannot
+hold a step's expert bytes.
+
+One step = moe_route_split (usage counter on) -> hot expert FFN (gate/up, down)
+on the main stream, cold expert FFN on a second stream -> moe_finalize; every
+64 steps the counter table is snapshotted (moe_usage_counts) at a drained
+barrier, the adaptive policy runs with the pages' defaults, and the swaps it
+proposes are applied with moe_swap_rows before the next step. All inputs are
+resident (device / pinned) before the timed region.
+
+Prints one JSON line (see the keys below). `value` is the achieved HBM
+bandwidth of the whole step (algorithmic HBM bytes per step / wall time per
+step); `us_per_layer` is the same step time in microseconds. `roofline` covers
+the hot-bank gate/up kernel (the kernel that moves the most HBM bytes), timed
+with HIP events on its stream. `cpu_baseline` is the CPU oracle on sampled
+steps of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer µs/decode step + achieved HBM GB/s (384e top-6 MXFP4, 1 GPU)"
+PEAK_HBM_GBPS = 8000.0
+NOMINAL_LINK_GBPS = 63.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--layers", type=int, default=8, help="distinct layer banks rotated through")
+    ap.add_argument("--tokens", type=int, default=16)
+    ap.add_argument("--map", default="fitted", choices=["fitted", "positional"])
+    ap.add_argument("--serial", action="store_true", help="cold FFN on the main stream")
+    ap.add_argument("--no-policy", action="store_true", help="no counter reads or swaps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--seed", type=int, default=20260917)
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------- ceilings --
+
+def _hip():
+    h = ctypes.CDLL("libamdhip64.so")
+    h.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p,
+                                          ctypes.c_uint]
+    return h
+
+
+def device_pointer(t):
+    """Device address of a pinned host tensor."""
+    p = ctypes.c_void_p()
+    rc = _hip().hipHostGetDevicePointer(ctypes.byref(p), ctypes.c_void_p(t.data_ptr()), 0)
+    if rc != 0:
+        raise RuntimeError(f"hipHostGetDevicePointer failed: {rc}")
+    return p.value
+
+
+def measure_ceilings(torch):
+    L = ctypes.CDLL(os.path.join(ROOT, "ceiling", "libceiling.so"))
+    L.ceiling_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_void_p]
+    L.ceiling_stream_read.restype = ctypes.c_int
+    blocks = 256 * 16
+    sink = torch.empty(blocks, dtype=torch.int64, device="cuda")
+    s = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        best = float("inf")
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            fn()
+            b.record(s)
+            b.synchronize()
+            best = min(best, a.elapsed_time(b) / 1e3)
+        return best
+
+    out = {}
+    dev = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    t = timed(lambda: L.ceiling_stream_read(dev.data_ptr(), dev.numel(), sink.data_ptr(), blocks,
+                                            ctypes.c_void_p(s.cuda_stream)), 5)
+    out["hbm_read_GBps"] = round(dev.numel() / t / 1e9, 1)
+    del dev
+    host = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    hp = device_pointer(host)
+    t = timed(lambda: L.ceiling_stream_read(hp, host.numel(), sink.data_ptr(), blocks,
+                                            ctypes.c_void_p(s.cuda_stream)), 3)
+    out["host_link_zero_copy_read_GBps"] = round(host.numel() / t / 1e9, 1)
+    dst = torch.empty(host.numel(), dtype=torch.uint8, device="cuda")
+    t = timed(lambda: dst.copy_(host, non_blocking=True), 3)
+    out["host_link_h2d_copy_GBps"] = round(host.numel() / t / 1e9, 1)
+    del host, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+# ----------------------------------------------------------------- main --
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the residency path runs on a single MI355X and this "
+              f"build has no multi-GPU path (--gpus {args.gpus}, WORLD_SIZE {world}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import expert_weight_residency_amd as moe
+    import synth
+    from expert_weight_residency_amd.layer import LayerBuffers
+    from expert_weight_residency_amd.policy import AdaptivePolicy
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.lib()
+    E, k, H, I, T = 384, 6, 4096, 2880, args.tokens
+    n_cold = 89
+    n_hot = E - n_cold
+    Lr, seed = args.layers, args.seed
+    sz = synth.expert_sizes(H, I)
+    b13, b2 = sz["w13"] + sz["s13"], sz["w2"] + sz["s2"]
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+
+    ceilings = {} if args.no_ceilings else measure_ceilings(torch)
+    log(f"ceilings {ceilings}")
+
+    # --- resident state: banks, maps, counters -------------------------------
+    hot, cold, maps_dev, maps_host, hot_owner, cold_owner = [], [], [], [], [], []
+    for l in range(Lr):
+        rm, ho, co = (synth.fitted_map(E, n_cold, seed, l) if args.map == "fitted"
+                      else synth.positional_map(E, n_cold))
+        hb = moe.Bank(*[torch.empty(s, dtype=torch.uint8, device="cuda")
+                        for s in synth.tensor_shapes(n_hot, H, I).values()], on_host=False)
+        synth.fill_bank_device(hb.tensors(), torch.from_numpy(ho).cuda(), seed, l, H, I)
+        cb = moe.Bank(*[torch.empty(s, dtype=torch.uint8, pin_memory=True)
+                        for s in synth.tensor_shapes(n_cold, H, I).values()], on_host=True)
+        synth.fill_bank_host(cb.tensors(), co, seed, l, H, I)
+        hot.append(hb)
+        cold.append(cb)
+        maps_host.append(rm.copy())
+        maps_dev.append(torch.from_numpy(rm.copy()).cuda())
+        hot_owner.append(ho.copy())
+        cold_owner.append(co.copy())
+    counts = torch.zeros((Lr, E), dtype=torch.int32, device="cuda")
+    snap = torch.empty((Lr, E), dtype=torch.int32, pin_memory=True)
+    staging = torch.empty(moe.moe_expert_bytes(H, I), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"{Lr} layer banks resident: {Lr * n_hot * (b13 + b2) / 2**30:.1f} GiB HBM, "
+        f"{Lr * n_cold * (b13 + b2) / 2**30:.1f} GiB pinned host")
+
+    # --- per-step inputs, generated and uploaded before timing ---------------
+    S = args.warmup + args.steps
+    ids_np = np.empty((S, T, k), np.int32)
+    w_np = np.empty((S, T, k), np.float32)
+    x_np = np.empty((S, T, H), np.uint16)
+    for s in range(S):
+        ids_np[s], w_np[s] = synth.skewed_routing(T, k, E, seed, s % Lr, s)
+        x_np[s] = synth.activations(T, H, seed, s % Lr, s)
+    ids_d = torch.from_numpy(ids_np).cuda()
+    w_d = torch.from_numpy(w_np).cuda()
+    x_d = torch.from_numpy(x_np.view(np.int16)).cuda()
+    bufs = LayerBuffers.allocate(T, k, H, I, n_hot, n_cold)
+    main_s = torch.cuda.Stream()
+    cold_s = main_s if args.serial else torch.cuda.Stream()
+    policy = AdaptivePolicy(Lr, E)
+    swaps = stale = 0
+
+    ev = {name: [] for name in ("gu0", "gu1", "dn1", "c0", "c1")}
+    bytes_step, hot_bytes_gu, cold_bytes, uh_list, uc_list, cold_picks = [], [], [], [], [], 0
+
+    def account(s, rm):
+        ids = ids_np[s]
+        m = rm[ids]
+        hot_ids, cold_ids = ids[m >= 0], ids[m < 0]
+        uh, uc = len(np.unique(hot_ids)), len(np.unique(cold_ids))
+        ph, pc = hot_ids.size, cold_ids.size
+        gu = uh * b13 + T * H * 2 + ph * I * 2
+        dn = uh * b2 + ph * I * 2 + ph * H * 2
+        cold_act = T * H * 2 + pc * I * 4 + pc * H * 2          # x read, h write+read, Y write
+        fin = T * k * H * 2 + T * k * 4 + T * H * 2
+        split = T * k * 4 + E * 4 + (T * k * 4) * 2
+        return gu, gu + dn + cold_act + fin + split, uc * (b13 + b2), uh, uc, pc
+
+    def step(s, timed):
+        l = s % Lr
+        moe.moe_route_split(ids_d[s], maps_dev[l], n_hot, n_cold, bufs.hot_split, bufs.cold_split,
+                            bufs.n_invalid, counts[l], 256, stream=main_s)
+        if cold_s is not main_s:
+            cold_s.wait_stream(main_s)
+        if timed:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(main_s)
+            ev["gu0"].append(e)
+        moe.moe_expert_gate_up_mxfp4(hot[l], bufs.hot_split, x_d[s], k, I, bufs.workspace,
+                                     stream=main_s)
+        if timed:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(main_s)
+            ev["gu1"].append(e)
+        moe.moe_expert_down_mxfp4(hot[l], bufs.hot_split, T, k, H, I, bufs.workspace, bufs.Y,
+                                  stream=main_s)
+        if timed:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(main_s)
+            ev["dn1"].append(e)
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(cold_s)
+            ev["c0"].append(e)
+        moe.moe_expert_ffn_mxfp4(cold[l], bufs.cold_split, x_d[s], k, I, bufs.workspace, bufs.Y,
+                                 stream=cold_s)
+        if timed:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(cold_s)
+            ev["c1"].append(e)
+        if cold_s is not main_s:
+            main_s.wait_stream(cold_s)
+        moe.moe_finalize(bufs.Y, w_d[s], bufs.out, stream=main_s)
+
+    def barrier():
+        nonlocal swaps, stale
+        moe.moe_usage_counts(counts, snap, stream=main_s)
+        main_s.synchronize()
+        policy.observe(snap.numpy())
+        for sw in policy.decide(hot_owner, cold_owner):
+            l = sw.layer
+            try:
+                moe.moe_swap_rows(hot[l], cold[l], sw.hot_row, sw.cold_row, sw.expect_hot_expert,
+                                  sw.expect_cold_expert, maps_dev[l], hot_owner[l], cold_owner[l],
+                                  staging, H, I, stream=main_s)
+            except moe.MoeStale:
+                stale += 1
+                continue
+            maps_host[l][sw.expect_hot_expert] = -1 - sw.cold_row
+            maps_host[l][sw.expect_cold_expert] = sw.hot_row
+            swaps += 1
+
+    with torch.cuda.stream(main_s):
+        for s in range(args.warmup):
+            step(s, False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            s = args.warmup + i
+            gu, tot, cb, uh, uc, pc = account(s, maps_host[s % Lr])
+            hot_bytes_gu.append(gu)
+            bytes_step.append(tot)
+            cold_bytes.append(cb)
+            uh_list.append(uh)
+            uc_list.append(uc)
+            cold_picks += pc
+            step(s, True)
+            if not args.no_policy and (s + 1) % policy.cfg.read_every == 0:
+                barrier()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+
+    K = args.steps
+    ms_per_step = (t1 - t0) * 1e3 / K
+    gu_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["gu0"], ev["gu1"])])
+    dn_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["gu1"], ev["dn1"])])
+    c_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["c0"], ev["c1"])])
+    achieved = float(np.sum(hot_bytes_gu) / (gu_ms.sum() / 1e3) / 1e9)
+    value = float(np.mean(bytes_step) / (ms_per_step / 1e3) / 1e9)
+    cold_link = float(np.sum(cold_bytes) / max(c_ms.sum() / 1e3, 1e-12) / 1e9)
+
+    # HBM traffic of the gate/up kernel from committed rocprofv3 counter runs
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic_gate_up_full_layer_decode_t16.json")
+    src = os.path.join(ROOT, "expert_weight_residency_amd", "csrc", "ffn_mxfp4.hip")
+    if os.path.exists(tpath):
+        rec = json.load(open(tpath))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("source_sha256") == sha:
+            traffic = rec.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"full_layer_decode_t{T}", "experts": E, "top_k": k, "hidden": H,
+                   "intermediate": I, "tokens": T, "hot_rows": n_hot, "cold_rows": n_cold,
+                   "weights": "mxfp4", "cold_bank": "pinned_host_in_place", "map": args.map,
+                   "layer_banks_rotated": Lr, "cold_stream": not args.serial,
+                   "policy": not args.no_policy},
+        "us_per_layer": round(ms_per_step * 1e3, 1),
+        "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
+        "hot_gate_up_us": round(float(gu_ms.mean() * 1e3), 1),
+        "hot_down_us": round(float(dn_ms.mean() * 1e3), 1),
+        "cold_ffn_us": round(float(c_ms.mean() * 1e3), 1),
+        "hot_ffn_GBps": round(float((np.sum(uh_list) * (b13 + b2)) / ((gu_ms.sum() + dn_ms.sum()) / 1e3) / 1e9), 1),
+        "cold_link": {"achieved_GBps": round(cold_link, 1),
+                      "ceiling_GBps": ceilings.get("host_link_zero_copy_read_GBps"),
+                      "nominal_GBps": NOMINAL_LINK_GBPS},
+        "routing": {"hot_unique_per_step": round(float(np.mean(uh_list)), 2),
+                    "cold_unique_per_step": round(float(np.mean(uc_list)), 2),
+                    "cold_share_of_picks": round(cold_picks / (K * T * k), 4)},
+        "swaps_applied": swaps, "swaps_stale": stale,
+        "ceilings": ceilings,
+        "roofline": {"kernel": "ffn_gate_up (hot bank)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E,
+                                              b13 + b2, account, log)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E, bexp, account, log):
+    """The oracle on sampled steps of the same workload (whole layer: all picks,
+    hot and cold, plus finalize), until about 10 s of CPU time."""
+    import oracle
+    import synth
+    t_tot, b_tot, n = 0.0, 0.0, 0
+    for s in range(args.warmup, args.warmup + min(args.steps, 4)):
+        l = s % Lr
+        ids = ids_np[s]
+        U = np.unique(ids)
+        bank = oracle.Bank(**synth.make_bank_host(U, args.seed, l, H, I))
+        rm = np.full(E, -(10 ** 6), np.int32)
+        rm[U] = np.arange(len(U), dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.moe_layer(bank, None, rm, ids, w_np[s], x_np[s], H, I)
+        t_tot += time.perf_counter() - t0
+        b_tot += account(s, maps_host[l])[1]
+        n += 1
+        if t_tot > 10.0:
+            break
+    per = t_tot / n
+    return {"value": round(b_tot / n / per / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "us_per_layer": round(per * 1e6, 1),
+            "sample": f"{n} of the timed steps (one full layer each: all {ids_np.shape[1]} tokens x "
+                      f"{ids_np.shape[2]} picks, hot and cold, plus finalize); same weights, "
+                      "routing and activations"}
+
+
+if __name__ == "__main__":
+    main()

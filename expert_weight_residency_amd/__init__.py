@@ -21,8 +21,8 @@ MOE_MAX_TOPK = 32
 
 # entry points declared in include/moe_residency.h
 ENTRY_POINTS = ("moe_expert_bytes", "moe_ffn_workspace_bytes", "moe_route_split",
-                "moe_expert_ffn_mxfp4", "moe_finalize", "moe_usage_counts", "moe_swap_rows",
-                "moe_last_error")
+                "moe_expert_ffn_mxfp4", "moe_expert_gate_up_mxfp4", "moe_expert_down_mxfp4",
+                "moe_finalize", "moe_usage_counts", "moe_swap_rows", "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -69,6 +69,12 @@ def lib():
         L.moe_expert_ffn_mxfp4.restype = i32
         L.moe_expert_ffn_mxfp4.argtypes = [ctypes.POINTER(MoeBankC), MoeSplitC, vp, i32, i32, i32,
                                            i32, vp, vp, vp]
+        L.moe_expert_gate_up_mxfp4.restype = i32
+        L.moe_expert_gate_up_mxfp4.argtypes = [ctypes.POINTER(MoeBankC), MoeSplitC, vp, i32, i32,
+                                               i32, i32, vp, vp]
+        L.moe_expert_down_mxfp4.restype = i32
+        L.moe_expert_down_mxfp4.argtypes = [ctypes.POINTER(MoeBankC), MoeSplitC, i32, i32, i32, i32,
+                                            vp, vp, vp]
         L.moe_finalize.restype = i32
         L.moe_finalize.argtypes = [vp, vp, i32, i32, i32, vp, vp]
         L.moe_usage_counts.restype = i32
@@ -178,6 +184,21 @@ def moe_expert_ffn_mxfp4(bank: Bank, split: Split, x, k: int, I: int, workspace,
     b = bank.abi()
     _check(lib().moe_expert_ffn_mxfp4(ctypes.byref(b), split.abi(), x.data_ptr(), T, k, H, I,
                                       workspace.data_ptr(), Y.data_ptr(), _stream(stream)))
+
+
+def moe_expert_gate_up_mxfp4(bank: Bank, split: Split, x, k: int, I: int, workspace,
+                             stream=None) -> None:
+    T, H = int(x.shape[0]), int(x.shape[1])
+    b = bank.abi()
+    _check(lib().moe_expert_gate_up_mxfp4(ctypes.byref(b), split.abi(), x.data_ptr(), T, k, H, I,
+                                          workspace.data_ptr(), _stream(stream)))
+
+
+def moe_expert_down_mxfp4(bank: Bank, split: Split, T: int, k: int, H: int, I: int, workspace, Y,
+                          stream=None) -> None:
+    b = bank.abi()
+    _check(lib().moe_expert_down_mxfp4(ctypes.byref(b), split.abi(), T, k, H, I,
+                                       workspace.data_ptr(), Y.data_ptr(), _stream(stream)))
 
 
 def moe_finalize(Y, topk_w, out, stream=None) -> None:

@@ -32,6 +32,8 @@ int check_dims(int T, int k, int H, int I) {
   if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_EINVAL, "T*k too large");
   if (H <= 0 || H % 64) return fail(MOE_EINVAL, "H=%d must be a positive multiple of 64", H);
   if (I <= 0 || I % 64) return fail(MOE_EINVAL, "I=%d must be a positive multiple of 64", I);
+  if (H > moe::ffn_max_reduction() || I > moe::ffn_max_reduction())
+    return fail(MOE_ENOTSUP, "H=%d, I=%d: at most %d supported", H, I, moe::ffn_max_reduction());
   return MOE_OK;
 }
 
@@ -104,25 +106,73 @@ int moe_route_split(const int32_t* topk_ids, int T, int k, const int32_t* row_ma
   return ok();
 }
 
-int moe_expert_ffn_mxfp4(const moe_bank* bank, moe_split split, const uint16_t* x, int T, int k,
-                         int H, int I, void* workspace, uint16_t* Y, void* stream) {
+// Shared checks of the three FFN entry points. Returns MOE_OK with *skip set
+// when there is nothing to launch.
+static int ffn_prepare(const moe_bank* bank, const moe_split& split, const void* x, int T, int k,
+                       int H, int I, const void* workspace, const void* Y, const uint8_t* p[4],
+                       int* cap, bool* skip) {
   int rc;
+  *skip = false;
   if ((rc = check_dims(T, k, H, I))) return rc;
   if (!bank) return fail(MOE_EINVAL, "bank is NULL");
   if (bank->n_rows < 0 || bank->n_rows > MOE_MAX_ROWS)
     return fail(MOE_EINVAL, "bank rows %d outside [0, %d]", bank->n_rows, MOE_MAX_ROWS);
-  if (T == 0 || bank->n_rows == 0) return ok();
+  if (T == 0 || bank->n_rows == 0) {
+    *skip = true;
+    return MOE_OK;
+  }
   if ((rc = check_split(split, "bank"))) return rc;
   if (!x || !workspace || !Y) return fail(MOE_EINVAL, "x, workspace and Y must not be NULL");
   if (!aligned16(x) || !aligned16(Y) || !aligned16(workspace))
     return fail(MOE_EINVAL, "x, workspace and Y must be 16-byte aligned");
-  const uint8_t* p[4];
   if ((rc = bank_device_ptrs(bank, p))) return rc;
   const int64_t picks = (int64_t)T * k;
-  const int cap = (int)(bank->n_rows < picks ? bank->n_rows : picks);
-  hipError_t e = moe::launch_ffn(p[0], p[1], p[2], p[3], cap, split, x, T, k, H, I,
-                                 static_cast<uint16_t*>(workspace), Y,
-                                 static_cast<hipStream_t>(stream));
+  *cap = (int)(bank->n_rows < picks ? bank->n_rows : picks);
+  return MOE_OK;
+}
+
+int moe_expert_gate_up_mxfp4(const moe_bank* bank, moe_split split, const uint16_t* x, int T,
+                             int k, int H, int I, void* workspace, void* stream) {
+  const uint8_t* p[4];
+  int cap = 0, rc;
+  bool skip;
+  // Y is not touched by this stage; pass x to satisfy the shared check
+  if ((rc = ffn_prepare(bank, split, x, T, k, H, I, workspace, x, p, &cap, &skip))) return rc;
+  if (skip) return ok();
+  hipError_t e = moe::launch_gate_up(p[0], p[1], cap, bank->on_host, split, x, T, k, H, I,
+                                     static_cast<uint16_t*>(workspace),
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_EHIP, "gate/up launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int moe_expert_down_mxfp4(const moe_bank* bank, moe_split split, int T, int k, int H, int I,
+                          const void* workspace, uint16_t* Y, void* stream) {
+  const uint8_t* p[4];
+  int cap = 0, rc;
+  bool skip;
+  // x is not read by this stage; pass the workspace to satisfy the shared check
+  if ((rc = ffn_prepare(bank, split, workspace, T, k, H, I, workspace, Y, p, &cap, &skip)))
+    return rc;
+  if (skip) return ok();
+  hipError_t e = moe::launch_down(p[2], p[3], cap, bank->on_host, split, T, H, I,
+                                  static_cast<const uint16_t*>(workspace), Y,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_EHIP, "down launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int moe_expert_ffn_mxfp4(const moe_bank* bank, moe_split split, const uint16_t* x, int T, int k,
+                         int H, int I, void* workspace, uint16_t* Y, void* stream) {
+  const uint8_t* p[4];
+  int cap = 0, rc;
+  bool skip;
+  if ((rc = ffn_prepare(bank, split, x, T, k, H, I, workspace, Y, p, &cap, &skip))) return rc;
+  if (skip) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* h = static_cast<uint16_t*>(workspace);
+  hipError_t e = moe::launch_gate_up(p[0], p[1], cap, bank->on_host, split, x, T, k, H, I, h, s);
+  if (e == hipSuccess) e = moe::launch_down(p[2], p[3], cap, bank->on_host, split, T, H, I, h, Y, s);
   if (e != hipSuccess) return fail(MOE_EHIP, "expert FFN launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -29,15 +29,25 @@ hipError_t launch_route_split(const int32_t* ids, int T, int k, const int32_t* r
                               const moe_split& hot, const moe_split& cold, int32_t* n_invalid,
                               hipStream_t stream);
 
-hipError_t launch_ffn(const uint8_t* w13, const uint8_t* s13, const uint8_t* w2,
-                      const uint8_t* s2, int cap, const moe_split& split, const uint16_t* x, int T,
-                      int k, int H, int I, uint16_t* h_ws, uint16_t* Y, hipStream_t stream);
+// cap: launch capacity in active rows (min(bank rows, T*k)); on_host: the
+// bank is in host memory (caps the wavefronts that read it at once).
+hipError_t launch_gate_up(const uint8_t* w13, const uint8_t* s13, int cap, int on_host,
+                          const moe_split& split, const uint16_t* x, int T, int k, int H, int I,
+                          uint16_t* h_ws, hipStream_t stream);
+
+hipError_t launch_down(const uint8_t* w2, const uint8_t* s2, int cap, int on_host,
+                       const moe_split& split, int T, int H, int I, const uint16_t* h_ws,
+                       uint16_t* Y, hipStream_t stream);
 
 hipError_t launch_finalize(const uint16_t* Y, const float* w, int T, int k, int H, uint16_t* out,
                            hipStream_t stream);
 
 hipError_t launch_map_write(int32_t* row_map, int e_a, int v_a, int e_b, int v_b,
                             hipStream_t stream);
+
+// Longest reduction axis (H or I) the expert FFN supports (one token row must
+// fit its LDS activation tile).
+int ffn_max_reduction();
 
 // Largest pick count handled by the single-kernel split.
 constexpr int kSplitSingleMaxPicks = 2048;

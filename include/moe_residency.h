@@ -41,7 +41,8 @@
  *    unweighted expert row per slot.
  *
  * Shape limits: 1 <= E <= MOE_MAX_EXPERTS; bank rows <= MOE_MAX_ROWS; H and I
- * positive multiples of 64; 1 <= k <= MOE_MAX_TOPK; T >= 0 and T*k < 2^31.
+ * positive multiples of 64, at most 32768; 1 <= k <= MOE_MAX_TOPK; T >= 0 and
+ * T*k < 2^31.
  * Pointers to weights, activations and Y rows must be 16-byte aligned.
  */
 #ifndef MOE_RESIDENCY_H
@@ -152,6 +153,19 @@ int moe_route_split(const int32_t *topk_ids, int T, int k, const int32_t *row_ma
  */
 int moe_expert_ffn_mxfp4(const moe_bank *bank, moe_split split, const uint16_t *x, int T, int k,
                          int H, int I, void *workspace, uint16_t *Y, void *stream);
+
+/*
+ * moe_expert_gate_up_mxfp4 / moe_expert_down_mxfp4 -- the two launches of
+ * moe_expert_ffn_mxfp4, callable one at a time (for timing each kernel, or to
+ * schedule them separately). gate_up writes h = silu(g) * u as bf16 into the
+ * workspace for this bank's slots; down reads it and writes this bank's rows
+ * of Y. moe_expert_ffn_mxfp4 is exactly gate_up followed by down, and the two
+ * paths give identical bits. Arguments as for moe_expert_ffn_mxfp4.
+ */
+int moe_expert_gate_up_mxfp4(const moe_bank *bank, moe_split split, const uint16_t *x, int T,
+                             int k, int H, int I, void *workspace, void *stream);
+int moe_expert_down_mxfp4(const moe_bank *bank, moe_split split, int T, int k, int H, int I,
+                          const void *workspace, uint16_t *Y, void *stream);
 
 /*
  * moe_finalize -- ordered fp32 FMA combine of the k rows of each token.

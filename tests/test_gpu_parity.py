@@ -263,3 +263,24 @@ def test_empty_step_writes_nothing():
     rm, ho, co, hot, cold, ids, w, x = _layer_case(E, k, H, I, 4, 4, 3, "gaussian")
     Y, out, ninv = run_layer(device_bank(hot), device_bank(cold), rm, ids[:0], w[:0], x[:0], H, I)
     assert ninv == 0 and Y.size == 0 and out.size == 0
+
+
+def test_stage_calls_equal_fused_call():
+    """moe_expert_gate_up_mxfp4 then moe_expert_down_mxfp4 == moe_expert_ffn_mxfp4, bitwise."""
+    E, k, H, I, T = 24, 3, 512, 320, 20
+    rm, ho, co, hot, cold, ids, w, x = _layer_case(E, k, H, I, T, 6, 13, "skewed")
+    bank = device_bank(hot)
+    ids_d, w_d, x_d = routing_tensors(ids, w, x)
+    rm_d = torch.from_numpy(rm).cuda()
+    hs, cs = moe.Split.empty(len(ho), T, k), moe.Split.empty(len(co), T, k)
+    ninv = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.moe_route_split(ids_d, rm_d, len(ho), len(co), hs, cs, ninv)
+    ws = torch.empty(moe.moe_ffn_workspace_bytes(T, k, I), dtype=torch.uint8, device="cuda")
+    Y1 = torch.zeros((T * k, H), dtype=torch.int16, device="cuda")
+    Y2 = torch.zeros((T * k, H), dtype=torch.int16, device="cuda")
+    moe.moe_expert_ffn_mxfp4(bank, hs, x_d, k, I, ws, Y1)
+    moe.moe_expert_gate_up_mxfp4(bank, hs, x_d, k, I, ws)
+    moe.moe_expert_down_mxfp4(bank, hs, T, k, H, I, ws, Y2)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+    assert int((Y1 != 0).any(dim=1).sum()) == int(hs.to_host()[1][-1])
