@@ -9,8 +9,8 @@
 // Built the Counter", section 1).
 //
 // Design for decode, where the layer is bound by streaming expert weights:
-//  - A workgroup of kWaves wavefronts owns one active row (expert) and a block
-//    of its weight rows; each wavefront owns 2 groups of 16 rows and walks the
+//  - A workgroup of 8 wavefronts owns one active row (expert) and a block of
+//    its weight rows; each wavefront owns 2 groups of 16 rows and walks the
 //    whole reduction axis, so each weight byte is read from HBM once per step
 //    (the pages' kernel re-reads an expert for every extra 8-token tile: "We
 //    Built the Counter", section 6).
@@ -44,19 +44,23 @@
 namespace moe {
 namespace {
 
-constexpr int kWaves = 8;         // wavefronts per workgroup
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWavesDevice = 8;   // wavefronts per workgroup (device bank)
+constexpr int kWavesHost = 8;     // ... and for a host-resident bank
 constexpr int kTT = 8;            // most tokens staged per pass
 constexpr int kLdsTile = 65536;   // LDS bytes of the activation tile
-constexpr int kP = 2;             // weight chunks in flight per wavefront
+constexpr int kPDevice = 2;       // weight chunks in flight per wavefront (device bank)
+constexpr int kPHost = 4;         // ... and for a host-resident bank (few wavefronts)
 constexpr int kNG = 2;            // 16-row MFMA groups per wavefront
 constexpr int kChunkElems = 256;  // reduction elements per chunk per row
 constexpr int kChunkBlocks = 8;   // E8M0 blocks per chunk
-// (4 waves per SIMD: two 8-wave workgroups per CU, 127 VGPRs, no spills.)
-// Wavefronts that read a host-resident bank at once. Host-link reads are slow
-// to return; with hundreds of wavefronts each holding several KB of them in
-// flight, they back up the memory path that concurrent HBM-bound kernels use.
-constexpr int kHostReadWaves = 32;
+// (Device banks: 4 waves per SIMD, two 8-wave workgroups per CU, no spills.)
+// Wavefronts that read a host-resident bank at once. Host-link reads in flight
+// beyond what saturates the link only back up the memory path that concurrent
+// HBM-bound kernels use, so the count is capped; with 4 chunks in flight per
+// wavefront, 64 wavefronts on 8 CUs reach ~42 GB/s while a concurrent hot-bank
+// kernel keeps ~95% of its speed. (Spreading the same wavefronts over 32 CUs
+// reads the link slightly faster but slows the hot bank 2.5x.)
+constexpr int kHostReadWaves = 64;
 
 struct AChunk {
   uint4 lo, hi;  // 64 E2M1 codes of one row: blocks 2q and 2q+1 of the chunk
@@ -114,7 +118,7 @@ __device__ __forceinline__ int lds_elem(int n, int kpad, int elem) {
 template <typename RowFn>
 __device__ __forceinline__ void stage_rows(__bf16* xs, int nvalid, int K, int kpad, RowFn src_row) {
   const int gpr = kpad / 8;  // granules per row
-  for (int gi = threadIdx.x; gi < nvalid * gpr; gi += kThreads) {
+  for (int gi = threadIdx.x; gi < nvalid * gpr; gi += blockDim.x) {
     const int n = gi / gpr, g = gi - n * gpr;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (g * 8 < K) v = *reinterpret_cast<const uint4*>(src_row(n) + g * 8);
@@ -123,9 +127,11 @@ __device__ __forceinline__ void stage_rows(__bf16* xs, int nvalid, int K, int kp
 }
 
 // acc[g] += W[group g] (16 x K, MXFP4) . B (K x 16 tokens, bf16 in LDS) over
-// the whole reduction axis, with kP chunks of weights in flight in a register
-// ring (indexed statically: the chunk loop is unrolled by kP + 1). nrow: LDS
+// the whole reduction axis, with P chunks of weights in flight in a register
+// ring (indexed statically: the chunk loop is unrolled by P + 1). P does not
+// change the arithmetic, only how far ahead the loads run. nrow: LDS
 // row this lane's token column reads (its token, or row 0 when it has none).
+template <int kP>
 __device__ __forceinline__ void mx_gemm(const uint8_t* const* wrow, const uint8_t* const* srow,
                                         int nblk, const __bf16* xs, int kpad, int nrow, int q,
                                         f32x4 (&acc)[kNG]) {
@@ -169,9 +175,10 @@ __device__ __forceinline__ void mx_gemm(const uint8_t* const* wrow, const uint8_
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 // Kernel 1: h[s][i] = silu(gate_i . x_t) * (up_i . x_t) for the slots of each
-// active row. Work item = kWaves wavefronts of one active row; wavefront w of
-// block b owns i-rows i0 = (b * kWaves + w) * 16 .. i0 + 15 (gate and up).
-__global__ __launch_bounds__(kThreads, 4) void ffn_gate_up(
+// active row. Work item = kW wavefronts of one active row; wavefront w of
+// block b owns i-rows i0 = (b * kW + w) * 16 .. i0 + 15 (gate and up).
+template <int kP, int kW>
+__global__ __launch_bounds__(64 * kW, kP <= 2 ? 4 : 2) void ffn_gate_up(
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
     const int32_t* __restrict__ n_active, const int32_t* __restrict__ active_rows,
     const int32_t* __restrict__ row_off, const int32_t* __restrict__ slots,
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up(
   const int nblk = H / 32;
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int a = item / blocks_per_row;
-    const int i0 = ((item % blocks_per_row) * kWaves + (threadIdx.x >> 6)) * 16;
+    const int i0 = ((item % blocks_per_row) * kW + (threadIdx.x >> 6)) * 16;
     const bool busy = i0 < I;
     const size_t row = active_rows[a];
     const uint8_t* wexp = w13 + row * (2 * (size_t)I) * wrb;
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up(
       __syncthreads();
       if (busy) {
         f32x4 acc[kNG] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        mx_gemm(wrow, srow, nblk, xs, kpad, r < nvalid ? r : 0, q, acc);
+        mx_gemm<kP>(wrow, srow, nblk, xs, kpad, r < nvalid ? r : 0, q, acc);
         // lane (r, q) holds i-rows i0 + 4q + v of token r
         if (r < nvalid) {
           uint32_t hb[4];
@@ -217,10 +224,11 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up(
   }
 }
 
-// Kernel 2: Y[s][o] = bf16(down_o . h_s). Work item = kWaves wavefronts of one
-// active row; wavefront w of block b owns output rows o0 = (b * kWaves + w) *
+// Kernel 2: Y[s][o] = bf16(down_o . h_s). Work item = kW wavefronts of one
+// active row; wavefront w of block b owns output rows o0 = (b * kW + w) *
 // 32 .. o0 + 31.
-__global__ __launch_bounds__(kThreads, 4) void ffn_down(
+template <int kP, int kW>
+__global__ __launch_bounds__(64 * kW, kP <= 2 ? 4 : 2) void ffn_down(
     const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
     const int32_t* __restrict__ n_active, const int32_t* __restrict__ active_rows,
     const int32_t* __restrict__ row_off, const int32_t* __restrict__ slots,
@@ -236,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_down(
   const __bf16* hb = reinterpret_cast<const __bf16*>(h_ws);
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int a = item / blocks_per_row;
-    const int o0 = ((item % blocks_per_row) * kWaves + (threadIdx.x >> 6)) * 16 * kNG;
+    const int o0 = ((item % blocks_per_row) * kW + (threadIdx.x >> 6)) * 16 * kNG;
     const bool busy = o0 < H;
     const size_t row = active_rows[a];
     const uint8_t* wexp = w2 + row * (size_t)H * wrb;
@@ -252,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_down(
       __syncthreads();
       if (busy) {
         f32x4 acc[kNG] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        mx_gemm(wrow, srow, nblk, xs, kpad, r < nvalid ? r : 0, q, acc);
+        mx_gemm<kP>(wrow, srow, nblk, xs, kpad, r < nvalid ? r : 0, q, acc);
         if (r < nvalid) {
           const size_t ybase = (size_t)slots[t0 + r] * H + o0 + 4 * q;
 #pragma unroll
@@ -272,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_down(
 // Blocks launched for `items` work items: all of them for a device bank, at
 // most kHostReadWaves wavefronts' worth for a host-resident bank.
 unsigned grid_for(int items, int on_host) {
-  const int cap = kHostReadWaves / kWaves;
+  const int cap = kHostReadWaves / kWavesHost;
   return (unsigned)(on_host && items > cap ? cap : items);
 }
 
@@ -296,11 +304,13 @@ hipError_t launch_gate_up(const uint8_t* w13, const uint8_t* s13, int cap, int o
                           const moe_split& sp, const uint16_t* x, int T, int k, int H, int I,
                           uint16_t* h_ws, hipStream_t stream) {
   (void)T;
-  const int blocks = (I / 16 + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(ffn_gate_up, dim3(grid_for(cap * blocks, on_host)), dim3(kThreads),
-                     lds_bytes(H), stream, w13, s13, sp.n_active, sp.active_rows, sp.row_off,
-                     sp.slots, reinterpret_cast<const __bf16*>(x), k, H, I, blocks,
-                     tokens_per_pass(H), h_ws);
+  const int w = on_host ? kWavesHost : kWavesDevice;
+  const int blocks = (I / 16 + w - 1) / w;
+  auto kern = on_host ? ffn_gate_up<kPHost, kWavesHost> : ffn_gate_up<kPDevice, kWavesDevice>;
+  hipLaunchKernelGGL(kern, dim3(grid_for(cap * blocks, on_host)), dim3(64 * w), lds_bytes(H),
+                     stream, w13, s13, sp.n_active, sp.active_rows, sp.row_off, sp.slots,
+                     reinterpret_cast<const __bf16*>(x), k, H, I, blocks, tokens_per_pass(H),
+                     h_ws);
   return hipGetLastError();
 }
 
@@ -308,8 +318,10 @@ hipError_t launch_down(const uint8_t* w2, const uint8_t* s2, int cap, int on_hos
                        const moe_split& sp, int T, int H, int I, const uint16_t* h_ws, uint16_t* Y,
                        hipStream_t stream) {
   (void)T;
-  const int blocks = (H / (16 * kNG) + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(ffn_down, dim3(grid_for(cap * blocks, on_host)), dim3(kThreads), lds_bytes(I),
+  const int w = on_host ? kWavesHost : kWavesDevice;
+  const int blocks = (H / (16 * kNG) + w - 1) / w;
+  auto kern = on_host ? ffn_down<kPHost, kWavesHost> : ffn_down<kPDevice, kWavesDevice>;
+  hipLaunchKernelGGL(kern, dim3(grid_for(cap * blocks, on_host)), dim3(64 * w), lds_bytes(I),
                      stream, w2, s2, sp.n_active, sp.active_rows, sp.row_off, sp.slots, h_ws, H, I,
                      blocks, tokens_per_pass(I), Y);
   return hipGetLastError();
