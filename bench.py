@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--seed", type=int, default=20260917)
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill"],
+                    help="decode: the default line; prefill: one 4096-token chunk per step "
+                         "(counter off), reported with the hot bank's MFMA utilisation")
     return ap.parse_args()
 
 
@@ -137,6 +140,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.lib()
+    if args.workload == "prefill":
+        return run_prefill(args)
     E, k, H, I, T = 384, 6, 4096, 2880, args.tokens
     n_cold = 89
     n_hot = E - n_cold
@@ -338,6 +343,185 @@ def main():
         result["cpu_baseline"] = cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E,
                                               b13 + b2, account, log)
     print(json.dumps(result), flush=True)
+
+
+def make_layer_banks(torch, moe, synth, E, n_cold, H, I, Lr, seed, map_kind="fitted"):
+    """Per layer: hot bank (HBM, device-filled), cold bank (pinned host), maps."""
+    n_hot = E - n_cold
+    hot, cold, maps_host = [], [], []
+    for l in range(Lr):
+        rm, ho, co = (synth.fitted_map(E, n_cold, seed, l) if map_kind == "fitted"
+                      else synth.positional_map(E, n_cold))
+        hb = moe.Bank(*[torch.empty(s, dtype=torch.uint8, device="cuda")
+                        for s in synth.tensor_shapes(n_hot, H, I).values()], on_host=False)
+        synth.fill_bank_device(hb.tensors(), torch.from_numpy(ho).cuda(), seed, l, H, I)
+        cb = moe.Bank(*[torch.empty(s, dtype=torch.uint8, pin_memory=True)
+                        for s in synth.tensor_shapes(n_cold, H, I).values()], on_host=True)
+        synth.fill_bank_host(cb.tensors(), co, seed, l, H, I)
+        hot.append(hb)
+        cold.append(cb)
+        maps_host.append(rm.copy())
+    return hot, cold, maps_host
+
+
+def run_prefill(args):
+    """One 4096-token prefill chunk of the full layer per step: split (counter
+    off: more than 256 tokens), hot FFN on the main stream, cold FFN on a side
+    stream, finalize. The hot bank runs the token-tiled kernels; its MFMA
+    utilisation is reported against the dense bf16 peak, and its HBM rate
+    against 8 TB/s."""
+    import torch
+
+    import expert_weight_residency_amd as moe
+    import synth
+    from expert_weight_residency_amd.layer import LayerBuffers
+
+    E, k, H, I, T = 384, 6, 4096, 2880, 4096
+    n_cold = 89
+    n_hot = E - n_cold
+    Lr, seed = min(args.layers, 2), args.seed
+    sz = synth.expert_sizes(H, I)
+    b13, b2 = sz["w13"] + sz["s13"], sz["w2"] + sz["s2"]
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+    steps, warmup = min(args.steps, 16), min(args.warmup, 2)
+    hot, cold, maps_host = make_layer_banks(torch, moe, synth, E, n_cold, H, I, Lr, seed, args.map)
+    maps_dev = [torch.from_numpy(m.copy()).cuda() for m in maps_host]
+    S = warmup + steps
+    ids_np = np.empty((S, T, k), np.int32)
+    w_np = np.empty((S, T, k), np.float32)
+    x_d = torch.empty((S, T, H), dtype=torch.int16, device="cuda")
+    for s in range(S):
+        ids_np[s], w_np[s] = synth.skewed_routing(T, k, E, seed, s % Lr, s)
+        x_d[s] = torch.from_numpy(synth.activations(T, H, seed, s % Lr, s).view(np.int16)).cuda()
+    ids_d = torch.from_numpy(ids_np).cuda()
+    w_d = torch.from_numpy(w_np).cuda()
+    bufs = LayerBuffers.allocate(T, k, H, I, n_hot, n_cold)
+    main_s = torch.cuda.Stream()
+    cold_s = main_s if args.serial else torch.cuda.Stream()
+    torch.cuda.synchronize()
+    log(f"prefill: {Lr} layer banks resident, {S} steps of inputs uploaded")
+
+    ev = {n: [] for n in ("gu0", "gu1", "dn1", "c0", "c1")}
+
+    def rec(name, stream):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        ev[name].append(e)
+
+    def step(s, timed):
+        l = s % Lr
+        moe.moe_route_split(ids_d[s], maps_dev[l], n_hot, n_cold, bufs.hot_split,
+                            bufs.cold_split, bufs.n_invalid, None, 256, stream=main_s)
+        if cold_s is not main_s:
+            cold_s.wait_stream(main_s)
+        if timed:
+            rec("gu0", main_s)
+        moe.moe_expert_gate_up_mxfp4(hot[l], bufs.hot_split, x_d[s], k, I, bufs.workspace,
+                                     stream=main_s)
+        if timed:
+            rec("gu1", main_s)
+        moe.moe_expert_down_mxfp4(hot[l], bufs.hot_split, T, k, H, I, bufs.workspace, bufs.Y,
+                                  stream=main_s)
+        if timed:
+            rec("dn1", main_s)
+            rec("c0", cold_s)
+        moe.moe_expert_ffn_mxfp4(cold[l], bufs.cold_split, x_d[s], k, I, bufs.workspace, bufs.Y,
+                                 stream=cold_s)
+        if timed:
+            rec("c1", cold_s)
+        if cold_s is not main_s:
+            main_s.wait_stream(cold_s)
+        moe.moe_finalize(bufs.Y, w_d[s], bufs.out, stream=main_s)
+
+    with torch.cuda.stream(main_s):
+        for s in range(warmup):
+            step(s, False)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(warmup + i, True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+
+    ms = (t1 - t0) * 1e3 / steps
+    gu = np.array([a.elapsed_time(b) for a, b in zip(ev["gu0"], ev["gu1"])]) / 1e3
+    dn = np.array([a.elapsed_time(b) for a, b in zip(ev["gu1"], ev["dn1"])]) / 1e3
+    cf = np.array([a.elapsed_time(b) for a, b in zip(ev["c0"], ev["c1"])]) / 1e3
+    uh, uc, ph, pc = [], [], [], []
+    for i in range(steps):
+        s = warmup + i
+        m = maps_host[s % Lr][ids_np[s]]
+        uh.append(len(np.unique(ids_np[s][m >= 0])))
+        uc.append(len(np.unique(ids_np[s][m < 0])))
+        ph.append(int((m >= 0).sum()))
+        pc.append(int((m < 0).sum()))
+    uh, uc, ph, pc = map(np.array, (uh, uc, ph, pc))
+    fl_gu = 2.0 * ph * (2 * I) * H          # gate/up flops per step (hot)
+    fl_dn = 2.0 * ph * H * I
+    peak_bf16 = 2500.0                      # dense bf16 MFMA, TFLOP/s
+    tf_gu = float(fl_gu.sum() / gu.sum() / 1e12)
+    tf_dn = float(fl_dn.sum() / dn.sum() / 1e12)
+    tf_hot = float((fl_gu + fl_dn).sum() / (gu + dn).sum() / 1e12)
+    hbm_hot = float((uh * (b13 + b2)).sum() / (gu + dn).sum() / 1e9)
+    bytes_step = uh * (b13 + b2) + T * H * 2 * 2 + (ph + pc) * (I * 4 + H * 4) + T * H * 2
+    result = {
+        "metric": METRIC,
+        "value": round(float(np.mean(bytes_step) / (ms / 1e3) / 1e9), 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"full_layer_prefill_t{T}", "experts": E, "top_k": k,
+                   "hidden": H, "intermediate": I, "tokens": T, "hot_rows": n_hot,
+                   "cold_rows": n_cold, "weights": "mxfp4", "cold_bank": "pinned_host_in_place",
+                   "map": args.map, "layer_banks_rotated": Lr, "counter": False,
+                   "cold_stream": not args.serial},
+        "us_per_layer": round(ms * 1e3, 1),
+        "tokens_per_s": round(T / (ms / 1e3), 1),
+        "hot_gate_up_us": round(float(gu.mean() * 1e6), 1),
+        "hot_down_us": round(float(dn.mean() * 1e6), 1),
+        "cold_ffn_us": round(float(cf.mean() * 1e6), 1),
+        "hot_us": round(float((gu + dn).mean() * 1e6), 1),
+        "hot_tokens_per_s": round(float(T / (gu + dn).mean()), 1),
+        "mfma": {"kernel": "ffn_tiled (hot bank, gate/up + down)", "bound": "mfma",
+                 "achieved": round(tf_hot, 1), "peak": peak_bf16, "unit": "TFLOP/s",
+                 "frac": round(tf_hot / peak_bf16, 4), "gate_up_TFLOPs": round(tf_gu, 1),
+                 "down_TFLOPs": round(tf_dn, 1)},
+        "hot_hbm": {"achieved": round(hbm_hot, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": round(hbm_hot / PEAK_HBM_GBPS, 4)},
+        "cold_link_GBps": round(float((uc * (b13 + b2)).sum() / cf.sum() / 1e9), 1),
+        "routing": {"hot_unique_per_step": round(float(uh.mean()), 2),
+                    "cold_unique_per_step": round(float(uc.mean()), 2),
+                    "cold_share_of_picks": round(float(pc.sum() / (ph + pc).sum()), 4)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_prefill(args, ids_np[warmup], w_np[warmup],
+                                                      warmup % Lr, H, I, E, ms, log)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_prefill(args, ids, w, layer, H, I, E, gpu_ms, log):
+    """The oracle on the first 48 tokens of one timed prefill step (all their
+    picks, hot and cold, plus finalize), scaled linearly to the 4096 tokens."""
+    import oracle
+    import synth
+    n = 48
+    ids, w = ids[:n], w[:n]
+    x = synth.activations(4096, H, args.seed, layer, args.warmup)[:n]
+    U = np.unique(ids)
+    bank = oracle.Bank(**synth.make_bank_host(U, args.seed, layer, H, I))
+    rm = np.full(E, -(10 ** 6), np.int32)
+    rm[U] = np.arange(len(U), dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.moe_layer(bank, None, rm, ids, w, x, H, I)
+    dt = time.perf_counter() - t0
+    per_step = dt * 4096 / n
+    return {"value": round(4096 / per_step, 2), "unit": "tokens/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "ms_per_step": round(per_step * 1e3, 1),
+            "gpu_tokens_per_s": round(4096 / (gpu_ms / 1e3), 1),
+            "sample": f"first {n} of the 4096 tokens of one timed step ({ids.size} picks, hot "
+                      "and cold, plus finalize), time scaled by 4096/48"}
 
 
 def cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E, bexp, account, log):

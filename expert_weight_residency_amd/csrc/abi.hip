@@ -155,7 +155,7 @@ int moe_expert_down_mxfp4(const moe_bank* bank, moe_split split, int T, int k, i
   if ((rc = ffn_prepare(bank, split, workspace, T, k, H, I, workspace, Y, p, &cap, &skip)))
     return rc;
   if (skip) return ok();
-  hipError_t e = moe::launch_down(p[2], p[3], cap, bank->on_host, split, T, H, I,
+  hipError_t e = moe::launch_down(p[2], p[3], cap, bank->on_host, split, T, k, H, I,
                                   static_cast<const uint16_t*>(workspace), Y,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MOE_EHIP, "down launch: %s", hipGetErrorString(e));
@@ -172,7 +172,7 @@ int moe_expert_ffn_mxfp4(const moe_bank* bank, moe_split split, const uint16_t* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint16_t* h = static_cast<uint16_t*>(workspace);
   hipError_t e = moe::launch_gate_up(p[0], p[1], cap, bank->on_host, split, x, T, k, H, I, h, s);
-  if (e == hipSuccess) e = moe::launch_down(p[2], p[3], cap, bank->on_host, split, T, H, I, h, Y, s);
+  if (e == hipSuccess) e = moe::launch_down(p[2], p[3], cap, bank->on_host, split, T, k, H, I, h, Y, s);
   if (e != hipSuccess) return fail(MOE_EHIP, "expert FFN launch: %s", hipGetErrorString(e));
   return ok();
 }

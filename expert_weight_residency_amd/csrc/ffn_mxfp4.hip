@@ -40,9 +40,12 @@
 //  - Work items are (active row, row block); a grid-stride loop lets a bank in
 //    host memory run on a capped number of wavefronts (see kHostReadWaves).
 #include "internal.h"
+#include "mxfp4_common.h"
 
 namespace moe {
 namespace {
+
+using namespace mx;
 
 constexpr int kWavesDevice = 8;   // wavefronts per workgroup (device bank)
 constexpr int kWavesHost = 8;     // ... and for a host-resident bank
@@ -51,8 +54,6 @@ constexpr int kLdsTile = 65536;   // LDS bytes of the activation tile
 constexpr int kPDevice = 2;       // weight chunks in flight per wavefront (device bank)
 constexpr int kPHost = 4;         // ... and for a host-resident bank (few wavefronts)
 constexpr int kNG = 2;            // 16-row MFMA groups per wavefront
-constexpr int kChunkElems = 256;  // reduction elements per chunk per row
-constexpr int kChunkBlocks = 8;   // E8M0 blocks per chunk
 // (Device banks: 4 waves per SIMD, two 8-wave workgroups per CU, no spills.)
 // Wavefronts that read a host-resident bank at once. Host-link reads in flight
 // beyond what saturates the link only back up the memory path that concurrent
@@ -61,58 +62,6 @@ constexpr int kChunkBlocks = 8;   // E8M0 blocks per chunk
 // kernel keeps ~95% of its speed. (Spreading the same wavefronts over 32 CUs
 // reads the link slightly faster but slows the hot bank 2.5x.)
 constexpr int kHostReadWaves = 64;
-
-struct AChunk {
-  uint4 lo, hi;  // 64 E2M1 codes of one row: blocks 2q and 2q+1 of the chunk
-  uint32_t sc;   // their two E8M0 scale bytes
-};
-
-__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
-  // 2^(b-127) as an fp32 bit pattern; b = 0 is the subnormal 2^-127, 255 is NaN.
-  const uint32_t bits = b == 0 ? 0x00400000u : (b == 255 ? 0x7fc00000u : (b << 23));
-  return __uint_as_float(bits);
-}
-
-// Chunk c of this lane's weight row. K is a multiple of 64, so the lane's two
-// blocks are both in range or both past the end; past the end the lane reads
-// block 0 instead (in bounds). Nothing here inspects the loaded values, so
-// issuing a load never waits for it; the consumer substitutes unit scales for
-// out-of-range lanes, whose activations are LDS zero padding.
-__device__ __forceinline__ void load_a(AChunk& a, const uint8_t* __restrict__ wrow,
-                                       const uint8_t* __restrict__ srow, int c, int q, int nblk) {
-  const int b0 = c * kChunkBlocks + 2 * q;
-  const int bb = b0 < nblk ? b0 : 0;
-  const uint4* p = reinterpret_cast<const uint4*>(wrow + bb * 16);
-  a.lo = p[0];
-  a.hi = p[1];
-  a.sc = *reinterpret_cast<const uint16_t*>(srow + bb);
-}
-
-__device__ __forceinline__ uint32_t word_of(const AChunk& a, int m) {
-  const uint4& v = m < 4 ? a.lo : a.hi;
-  switch (m & 3) {
-    case 0: return v.x;
-    case 1: return v.y;
-    case 2: return v.z;
-    default: return v.w;
-  }
-}
-
-// 8 E2M1 codes (one dword, low nibble first) times a power-of-two scale -> 8 bf16.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t w, float s) {
-  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
-  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
-  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
-  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
-  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-// LDS activation tile: kTT rows of kpad elements; 16-byte granule g of row n
-// is stored at granule g ^ (n & 7), so the lanes of one MFMA operand read
-// (which differ in row and sit at the same column) hit different banks.
-__device__ __forceinline__ int lds_elem(int n, int kpad, int elem) {
-  return n * kpad + ((((elem >> 3) ^ (n & 7))) << 3);
-}
 
 // Stage rows src_row(n) for n < nvalid into the LDS tile, zero past K.
 template <typename RowFn>
@@ -156,10 +105,7 @@ __device__ __forceinline__ void mx_gemm(const uint8_t* const* wrow, const uint8_
       const int e0 = cc * kChunkElems + 64 * q;
       float sc[kNG][2];
 #pragma unroll
-      for (int g = 0; g < kNG; ++g) {
-        sc[g][0] = ok ? e8m0_to_f32(ring[u][g].sc & 0xffu) : 1.0f;
-        sc[g][1] = ok ? e8m0_to_f32((ring[u][g].sc >> 8) & 0xffu) : 1.0f;
-      }
+      for (int g = 0; g < kNG; ++g) chunk_scales(ring[u][g], ok, sc[g][0], sc[g][1]);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const bf16x8 bv = *reinterpret_cast<const bf16x8*>(xs + lds_elem(nrow, kpad, e0 + 8 * m));
@@ -172,7 +118,6 @@ __device__ __forceinline__ void mx_gemm(const uint8_t* const* wrow, const uint8_
   }
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 // Kernel 1: h[s][i] = silu(gate_i . x_t) * (up_i . x_t) for the slots of each
 // active row. Work item = kW wavefronts of one active row; wavefront w of
@@ -303,7 +248,8 @@ int ffn_max_reduction() { return kLdsTile / (int)sizeof(uint16_t); }
 hipError_t launch_gate_up(const uint8_t* w13, const uint8_t* s13, int cap, int on_host,
                           const moe_split& sp, const uint16_t* x, int T, int k, int H, int I,
                           uint16_t* h_ws, hipStream_t stream) {
-  (void)T;
+  if (ffn_use_tiled(T, k, cap))
+    return launch_gate_up_tiled(w13, s13, cap, on_host, sp, x, T, k, H, I, h_ws, stream);
   const int w = on_host ? kWavesHost : kWavesDevice;
   const int blocks = (I / 16 + w - 1) / w;
   auto kern = on_host ? ffn_gate_up<kPHost, kWavesHost> : ffn_gate_up<kPDevice, kWavesDevice>;
@@ -315,9 +261,10 @@ hipError_t launch_gate_up(const uint8_t* w13, const uint8_t* s13, int cap, int o
 }
 
 hipError_t launch_down(const uint8_t* w2, const uint8_t* s2, int cap, int on_host,
-                       const moe_split& sp, int T, int H, int I, const uint16_t* h_ws, uint16_t* Y,
-                       hipStream_t stream) {
-  (void)T;
+                       const moe_split& sp, int T, int k, int H, int I, const uint16_t* h_ws,
+                       uint16_t* Y, hipStream_t stream) {
+  if (ffn_use_tiled(T, k, cap))
+    return launch_down_tiled(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
   const int w = on_host ? kWavesHost : kWavesDevice;
   const int blocks = (H / (16 * kNG) + w - 1) / w;
   auto kern = on_host ? ffn_down<kPHost, kWavesHost> : ffn_down<kPDevice, kWavesDevice>;

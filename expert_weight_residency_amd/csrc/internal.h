@@ -36,8 +36,24 @@ hipError_t launch_gate_up(const uint8_t* w13, const uint8_t* s13, int cap, int o
                           uint16_t* h_ws, hipStream_t stream);
 
 hipError_t launch_down(const uint8_t* w2, const uint8_t* s2, int cap, int on_host,
-                       const moe_split& split, int T, int H, int I, const uint16_t* h_ws,
+                       const moe_split& split, int T, int k, int H, int I, const uint16_t* h_ws,
                        uint16_t* Y, hipStream_t stream);
+
+// Token-tiled kernels for steps with many picks per active row (ffn_tiled.hip);
+// launch_gate_up / launch_down hand over to them when ffn_use_tiled says so.
+// Both families give the same bits for every pick.
+hipError_t launch_gate_up_tiled(const uint8_t* w13, const uint8_t* s13, int cap, int on_host,
+                                const moe_split& split, const uint16_t* x, int T, int k, int H,
+                                int I, uint16_t* h_ws, hipStream_t stream);
+hipError_t launch_down_tiled(const uint8_t* w2, const uint8_t* s2, int cap, int on_host,
+                             const moe_split& split, int T, int k, int H, int I,
+                             const uint16_t* h_ws, uint16_t* Y, hipStream_t stream);
+
+// Average picks per launchable row from which the token-tiled kernels run.
+constexpr int kTiledMinPicksPerRow = 16;
+// Wavefronts that read a host-resident bank at once in the token-tiled kernels.
+constexpr int kTiledHostWaves = 64;
+bool ffn_use_tiled(int T, int k, int cap);
 
 hipError_t launch_finalize(const uint16_t* Y, const float* w, int T, int k, int H, uint16_t* out,
                            hipStream_t stream);
