@@ -1,0 +1,227 @@
+// Gate/up + SwiGLU for decode-sized steps with the activations resident in LDS
+// (gfx950). Same operation as the gate/up kernels in ffn_mxfp4.hip and
+// ffn_tiled.hip ("vLLM: Pin Hot Experts", section "Results, September 17":
+// the routed MXFP4 expert FFN per bank), organised so that a wavefront's
+// weight stream never drains:
+//
+//  - One workgroup of 16 wavefronts per CU. It stages every token row of x
+//    (T <= 16 rows of H) and the split's bookkeeping (active rows, offsets,
+//    the token of every slot) into LDS once, behind one barrier. After that
+//    no wavefront waits for another.
+//  - Work item = 16 i-columns of one active expert (its 16 gate rows and 16
+//    up rows). Each wavefront takes a contiguous run of items and streams
+//    their weight chunks back to back, kP chunks ahead in a register ring, so
+//    the prefetch runs straight across item boundaries. Inside the loop the
+//    only global loads are the weight chunks, issued unconditionally (past
+//    the wavefront's last item it re-reads that item's rows), so waiting for
+//    one chunk never waits for a newer one.
+//  - Exactly as many wavefronts run as make every run the same length
+//    (ceil(items / ceil(items / wavefronts))), so no wavefront has an extra
+//    item at the end; the idle ones are spread over the workgroups.
+//  - An item's tokens are the MFMA columns (16 per pass; an expert with more
+//    than 16 slots, which needs duplicate ids in a token, takes more passes).
+//  - Each output element sees the same MFMA sequence as in the other kernel
+//    families (same 256-element chunks, same lane-to-element map, same order
+//    from zero) and the same SwiGLU, so a pick gives the same bits.
+#include "internal.h"
+#include "mxfp4_common.h"
+
+namespace moe {
+namespace {
+
+using namespace mx;
+
+constexpr int kWaves = 16;               // wavefronts per workgroup (one workgroup per CU)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kNG = 2;                   // MFMA row groups per item (gate, up)
+
+// Bytes of LDS the kernel needs: activations, then int32 tables.
+size_t resident_lds_bytes(int T, int k, int H, int cap) {
+  const size_t kpad = (size_t)(H + kChunkElems - 1) / kChunkElems * kChunkElems;
+  return (size_t)T * kpad * sizeof(uint16_t) +
+         ((size_t)cap + (size_t)cap + 1 + 2 * (size_t)T * k) * sizeof(int32_t);
+}
+
+template <int P>
+__global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
+    const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
+    const int32_t* __restrict__ n_active, const int32_t* __restrict__ active_rows,
+    const int32_t* __restrict__ row_off, const int32_t* __restrict__ slots,
+    const __bf16* __restrict__ x, int T, int k, int H, int I, uint16_t* __restrict__ h_ws) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int kpad = (H + kChunkElems - 1) / kChunkElems * kChunkElems;
+  __bf16* xs = reinterpret_cast<__bf16*>(smem);
+  const int na = *n_active;
+  int* l_rows = reinterpret_cast<int*>(xs + (size_t)T * kpad);  // [na]
+  int* l_off = l_rows + na;                                     // [na + 1]
+  int* l_slot = l_off + na + 1;                                 // [T*k] slot ids, split order
+  int* l_tok = l_slot + T * k;                                  // [T*k] their tokens
+
+  const int tid = threadIdx.x;
+  const int picks = T * k;
+  {
+    const int gpr = kpad / 8;
+    for (int gi = tid; gi < T * gpr; gi += kThreads) {
+      const int n = gi / gpr, g = gi - n * gpr;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (g * 8 < H) v = *reinterpret_cast<const uint4*>(x + (size_t)n * H + g * 8);
+      *reinterpret_cast<uint4*>(xs + lds_elem(n, kpad, g * 8)) = v;
+    }
+    for (int i = tid; i < na; i += kThreads) l_rows[i] = active_rows[i];
+    for (int i = tid; i <= na; i += kThreads) l_off[i] = row_off[i];
+    const int nslots = na > 0 ? row_off[na] : 0;
+    for (int i = tid; i < nslots && i < picks; i += kThreads) {
+      const int sl = slots[i];
+      l_slot[i] = sl;
+      l_tok[i] = sl / k;
+    }
+  }
+  __syncthreads();
+
+  const int per = I / 16;  // items per expert
+  const int n = na * per;
+  if (n == 0) return;
+  const int W = gridDim.x * kWaves;
+  const int q_items = (n + W - 1) / W;
+  const int w_eff = (n + q_items - 1) / q_items;
+  // Everything that steers the loop is wave-uniform; readfirstlane keeps it in
+  // scalar registers (values read from LDS would otherwise count as per-lane
+  // and turn the loop into exec-masked control flow).
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wid = wv * gridDim.x + blockIdx.x;
+  if (wid >= w_eff) return;  // no barrier follows
+  const int it0 = wid * q_items;
+  const int it1 = min(n, it0 + q_items);
+
+  const int lane = tid & 63, r = lane & 15, q = lane >> 4;
+  const int nblk = H / 32, nchunk = (H + kChunkElems - 1) / kChunkElems;
+  const size_t wrb = H / 2, srb = H / 32;
+  const size_t rows_per_expert = 2 * (size_t)I;
+
+  // Number of 16-token passes of item `it`.
+  auto passes_of = [&](int it) {
+    const int a = it / per;
+    const int nt = __builtin_amdgcn_readfirstlane(l_off[a + 1] - l_off[a]);
+    return (nt + 15) >> 4;
+  };
+
+  // Prefetch cursor: item, pass, chunk, and this lane's two row pointers.
+  int p_it = it0, p_pass = 0, p_c = 0, p_npass = passes_of(it0);
+  const uint8_t* pw[kNG];
+  const uint8_t* ps[kNG];
+  auto p_rows = [&](int it) {
+    const int a = it / per, i0 = (it - a * per) * 16;
+    const size_t row = (uint32_t)__builtin_amdgcn_readfirstlane(l_rows[a]);
+    const uint8_t* wexp = w13 + row * rows_per_expert * wrb;
+    const uint8_t* sexp = s13 + row * rows_per_expert * srb;
+    pw[0] = wexp + (size_t)(i0 + r) * wrb;
+    ps[0] = sexp + (size_t)(i0 + r) * srb;
+    pw[1] = wexp + (size_t)(I + i0 + r) * wrb;
+    ps[1] = sexp + (size_t)(I + i0 + r) * srb;
+  };
+  p_rows(p_it);
+  auto p_advance = [&]() {
+    if (++p_c < nchunk) return;
+    p_c = 0;
+    if (++p_pass < p_npass) return;
+    p_pass = 0;
+    if (p_it + 1 < it1) {
+      ++p_it;
+      p_rows(p_it);
+      p_npass = passes_of(p_it);
+    }
+  };
+
+  AChunk ring[P + 1][kNG];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+#pragma unroll
+    for (int g = 0; g < kNG; ++g) load_a(ring[p][g], pw[g], ps[g], p_c, q, nblk);
+    p_advance();
+  }
+
+  // Items (and their 16-token passes) in order; nchunk is a multiple of P + 1,
+  // so every pass starts at ring slot 0 and the prefetch cursor, P chunks
+  // ahead, crosses into the next pass without a pause.
+  for (int it = it0; it < it1; ++it) {
+    const int a = it / per, i0 = (it - a * per) * 16;
+    const int beg = __builtin_amdgcn_readfirstlane(l_off[a]);
+    const int nt = __builtin_amdgcn_readfirstlane(l_off[a + 1]) - beg;
+    for (int pass = 0; pass * 16 < nt; ++pass) {
+      const int j = pass * 16 + r;
+      const bool has = j < nt;
+      const int xrow = l_tok[beg + (has ? j : 0)];
+      f32x4 acc[kNG] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      for (int c = 0; c < nchunk; c += P + 1) {
+#pragma unroll
+        for (int u = 0; u <= P; ++u) {
+          const int cc = c + u;
+#pragma unroll
+          for (int g = 0; g < kNG; ++g)
+            load_a(ring[(u + P) % (P + 1)][g], pw[g], ps[g], p_c, q, nblk);
+          p_advance();
+          const bool ok = cc * kChunkBlocks + 2 * q < nblk;
+          float sc[kNG][2];
+#pragma unroll
+          for (int g = 0; g < kNG; ++g) chunk_scales(ring[u][g], ok, sc[g][0], sc[g][1]);
+          const int e0 = cc * kChunkElems + 64 * q;
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const bf16x8 bv =
+                *reinterpret_cast<const bf16x8*>(xs + lds_elem(xrow, kpad, e0 + 8 * m));
+#pragma unroll
+            for (int g = 0; g < kNG; ++g)
+              acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  dequant8(word_of(ring[u][g], m), sc[g][m >> 2]), bv, acc[g], 0, 0, 0);
+          }
+        }
+      }
+      // lane (r, q) holds i-rows i0 + 4q + v of the pass's token r
+      if (has) {
+        const size_t sl = l_slot[beg + j];
+        uint32_t hb[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) hb[v] = f32_to_bf16_bits(silu_f32(acc[0][v]) * acc[1][v]);
+        *reinterpret_cast<uint2*>(h_ws + sl * I + i0 + 4 * q) =
+            make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+      }
+    }
+  }
+}
+
+template <int P>
+hipError_t launch_p(const uint8_t* w13, const uint8_t* s13, int cap, const moe_split& sp,
+                    const uint16_t* x, int T, int k, int H, int I, uint16_t* h_ws,
+                    hipStream_t stream, int cus) {
+  hipLaunchKernelGGL(ffn_gate_up_resident<P>, dim3(cus), dim3(kThreads),
+                     resident_lds_bytes(T, k, H, cap), stream, w13, s13, sp.n_active,
+                     sp.active_rows, sp.row_off, sp.slots, reinterpret_cast<const __bf16*>(x), T,
+                     k, H, I, h_ws);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool ffn_use_resident(int T, int k, int H, int cap, int on_host) {
+  return !on_host && T >= 1 && T <= 16 && resident_lds_bytes(T, k, H, cap) <= kResidentMaxLds;
+}
+
+hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int cap,
+                                   const moe_split& sp, const uint16_t* x, int T, int k, int H,
+                                   int I, uint16_t* h_ws, hipStream_t stream) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  // The deepest ring whose length divides the chunk count.
+  const int nchunk = (H + kChunkElems - 1) / kChunkElems;
+  if (nchunk % 4 == 0) return launch_p<3>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, cus);
+  if (nchunk % 3 == 0) return launch_p<2>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, cus);
+  if (nchunk % 2 == 0) return launch_p<1>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, cus);
+  return launch_p<0>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, cus);
+}
+
+}  // namespace moe

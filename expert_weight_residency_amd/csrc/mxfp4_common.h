@@ -64,11 +64,15 @@ __device__ __forceinline__ int lds_elem(int n, int kpad, int elem) {
   return n * kpad + ((((elem >> 3) ^ (n & 7))) << 3);
 }
 
-// Scales of a lane's two blocks in a chunk; unit past the end of the axis
-// (the lane then read an in-bounds block whose activations are zero).
+// Scales of a lane's two blocks in a chunk; unit (byte 127) past the end of
+// the axis (the lane then read an in-bounds block whose activations are zero).
+// The byte is selected before the conversion so that no branch forms around
+// the loaded value (a branch there makes the compiler wait for every load in
+// flight, not just this chunk's).
 __device__ __forceinline__ void chunk_scales(const AChunk& a, bool ok, float& s0, float& s1) {
-  s0 = ok ? e8m0_to_f32(a.sc & 0xffu) : 1.0f;
-  s1 = ok ? e8m0_to_f32((a.sc >> 8) & 0xffu) : 1.0f;
+  const uint32_t b = ok ? (uint32_t)a.sc : 0x7f7fu;
+  s0 = e8m0_to_f32(b & 0xffu);
+  s1 = e8m0_to_f32(b >> 8);
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }

@@ -1,0 +1,99 @@
+"""GPU parity of the gate/up kernel with all activations resident in LDS.
+
+The library runs it for device-resident banks when 1 <= T <= 16 (decode). It
+must match the oracle within tolerance (relative L2 <= 1e-2, max relative <=
+3e-2, every slot on its own) and give the same bits as the other kernel
+families for every pick:
+  - decode shapes (T = 1, 7, 16 at full H = 4096, I = 2880; a ragged I);
+  - an expert picked by all 16 tokens (one full 16-token pass) and an expert
+    with 64 slots from duplicate ids (four passes);
+  - bitwise against the host-bank path (the decode kernel: a cold bank in
+    pinned memory never uses this kernel) and the token-tiled path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import expert_weight_residency_amd as moe
+import oracle
+import synth
+from gpu_util import (MAX_REL, REL_L2, device_bank, host_bank, oracle_bank, pinned_bank,
+                      rel_errors, run_layer)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.lib()
+    yield
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def _check(rm, hot, cold, ids, w, x, H, I, cold_pinned=False):
+    T, k = ids.shape
+    Yr, outr, bad = oracle.moe_layer(oracle_bank(hot), oracle_bank(cold), rm, ids, w, x, H, I)
+    assert bad == 0
+    cb = pinned_bank(cold) if cold_pinned else device_bank(cold)
+    Y, out, ninv = run_layer(device_bank(hot), cb, rm, ids, w, x, H, I)
+    assert ninv == 0
+    Yr = Yr.reshape(T * k, H)
+    e_y, e_o = rel_errors(Y, Yr), rel_errors(out, outr)
+    log(f"  Y rel-L2 {e_y[0]:.2e} max-rel {e_y[1]:.2e}; out rel-L2 {e_o[0]:.2e} max-rel {e_o[1]:.2e}")
+    assert e_y[0] <= REL_L2 and e_y[1] <= MAX_REL
+    assert e_o[0] <= REL_L2 and e_o[1] <= MAX_REL
+    for s in range(T * k):
+        r = rel_errors(Y[s], Yr[s])
+        assert r[0] <= REL_L2, (s, r)
+    return Y
+
+
+@pytest.mark.parametrize("shape", [(48, 6, 4096, 2880, 1), (48, 6, 4096, 2880, 7),
+                                   (48, 6, 4096, 2880, 16), (24, 4, 1024, 320, 16)],
+                         ids=["T1", "T7", "T16", "I320_T16"])
+def test_resident_matches_oracle(shape):
+    E, k, H, I, T = shape
+    log(f"resident {shape}")
+    rm, ho, co = synth.random_map(E, E // 4, 7)
+    hot, cold = host_bank(ho, 7, 0, H, I), host_bank(co, 7, 0, H, I)
+    ids, w = synth.skewed_routing(T, k, E, 7, 0, 0)
+    x = synth.activations(T, H, 7)
+    _check(rm, hot, cold, ids, w, x, H, I)
+
+
+def test_resident_full_pass_and_duplicates():
+    """Expert 2 in every token's picks (16 slots: one full pass); expert 5 in
+    every pick of tokens 0..15 of a second call (64 slots: four passes)."""
+    E, k, H, I, T = 8, 4, 512, 256, 16
+    rm, ho, co = synth.map_from_cold_set(E, [7])
+    hot, cold = host_bank(ho, 9, 0, H, I), host_bank(co, 9, 0, H, I)
+    x = synth.activations(T, H, 9)
+    ids, w = synth.gaussian_routing(T, k, E, 9)
+    for t in range(T):
+        if 2 not in ids[t]:
+            ids[t, t % k] = 2
+    log("resident: expert with 16 slots")
+    _check(rm, hot, cold, ids, w, x, H, I)
+    ids_dup = np.full((T, k), 5, np.int32)
+    log("resident: expert with 64 slots (duplicate ids)")
+    _check(rm, hot, cold, ids_dup, np.full((T, k), 0.25, np.float32), x, H, I)
+
+
+@pytest.mark.parametrize("T", [4, 16])
+def test_resident_equals_host_bank_path_bitwise(T):
+    """Every expert once in HBM (resident kernel) and once in pinned host
+    memory (decode kernel): identical Y rows."""
+    E, k, H, I = 16, 2, 4096, 2880
+    all_map, owners, _ = synth.all_hot_map(E)
+    arrays = host_bank(owners, 13, 0, H, I)
+    ids, w = synth.gaussian_routing(T, k, E, 13)
+    x = synth.activations(T, H, 13)
+    Yd, _, _ = run_layer(device_bank(arrays), None, all_map, ids, w, x, H, I)
+    cold_map = -1 - all_map  # every expert cold, same rows
+    empty = host_bank(np.zeros(0, np.int32), 13, 0, H, I)
+    Yh, _, _ = run_layer(device_bank(empty), pinned_bank(arrays), cold_map, ids, w, x, H, I)
+    assert np.array_equal(Yd, Yh)
