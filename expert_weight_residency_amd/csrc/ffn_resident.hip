@@ -18,6 +18,11 @@
 //  - Exactly as many wavefronts run as make every run the same length
 //    (ceil(items / ceil(items / wavefronts))), so no wavefront has an extra
 //    item at the end; the idle ones are spread over the workgroups.
+//  - Scale bytes are loaded once per 4 chunks per row group (8 bytes per
+//    lane, one chunk's scales each) and redistributed across the lane
+//    quarters with two lane-swap instructions: a per-chunk 2-byte load per
+//    lane costs a whole memory instruction for 1/16 of the bytes, and those
+//    instructions, not the bytes, bounded this kernel.
 //  - An item's tokens are the MFMA columns (16 per pass; an expert with more
 //    than 16 slots, which needs duplicate ids in a token, takes more passes).
 //  - Each output element sees the same MFMA sequence as in the other kernel
@@ -40,6 +45,29 @@ size_t resident_lds_bytes(int T, int k, int H, int cap) {
   const size_t kpad = (size_t)(H + kChunkElems - 1) / kChunkElems * kChunkElems;
   return (size_t)T * kpad * sizeof(uint16_t) +
          ((size_t)cap + (size_t)cap + 1 + 2 * (size_t)T * k) * sizeof(int32_t);
+}
+
+// This lane's 64 E2M1 codes of chunk c of a row (blocks 2q and 2q+1).
+__device__ __forceinline__ void load_w(AChunk& a, const uint8_t* __restrict__ wrow, int c, int q) {
+  const uint4* p = reinterpret_cast<const uint4*>(wrow + c * 128 + 32 * q);
+  a.lo = p[0];
+  a.hi = p[1];
+}
+
+// Lane (r, q) holds raw = the 8 scale bytes of chunk c0 + q of its row r
+// (pair j = bytes 2j, 2j+1 belongs to lane quarter j). Transpose the 4 x 4
+// pairs across the four lane quarters (lanes r, r+16, r+32, r+48): afterwards
+// lane (r, q) holds its own pair of chunks c0 .. c0+3 as x.lo, y.lo, x.hi,
+// y.hi. permlane32_swap(a, b) exchanges a's lanes 32-63 with b's lanes 0-31;
+// permlane16_swap(a, b) exchanges a's odd 16-lane rows with b's even rows.
+__device__ __forceinline__ void scale_quad(uint2 raw, uint32_t& x, uint32_t& y) {
+  const auto h = __builtin_amdgcn_permlane32_swap(raw.x, raw.y, false, false);
+  const uint32_t lo = h[0], hi = h[1];
+  const uint32_t px = __builtin_amdgcn_perm(hi, lo, 0x05040100u);  // lo.low16, hi.low16
+  const uint32_t py = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // lo.high16, hi.high16
+  const auto v = __builtin_amdgcn_permlane16_swap(px, py, false, false);
+  x = v[0];
+  y = v[1];
 }
 
 template <int P>
@@ -94,7 +122,7 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
   const int it1 = min(n, it0 + q_items);
 
   const int lane = tid & 63, r = lane & 15, q = lane >> 4;
-  const int nblk = H / 32, nchunk = (H + kChunkElems - 1) / kChunkElems;
+  const int nchunk = H / kChunkElems;  // H is a multiple of 1024
   const size_t wrb = H / 2, srb = H / 32;
   const size_t rows_per_expert = 2 * (size_t)I;
 
@@ -132,17 +160,27 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
     }
   };
 
+  // Weight chunks run P ahead in a ring of P + 1 = 4 (only lo/hi of AChunk are
+  // used). Scale bytes come in quads: at the start of every 4 chunks each
+  // lane loads the 8 scale bytes of one of the next 4 chunks of its row, and
+  // scale_quad turns them into this lane's own pairs, so a wavefront issues
+  // one scale load per row group per 4 chunks instead of one per chunk.
+  static_assert(P == 3, "the ring cycle must match the 4-chunk scale quad");
   AChunk ring[P + 1][kNG];
+  uint2 sraw[kNG];
+#pragma unroll
+  for (int g = 0; g < kNG; ++g)
+    sraw[g] = *reinterpret_cast<const uint2*>(ps[g] + 8 * (p_c + q));
 #pragma unroll
   for (int p = 0; p < P; ++p) {
 #pragma unroll
-    for (int g = 0; g < kNG; ++g) load_a(ring[p][g], pw[g], ps[g], p_c, q, nblk);
+    for (int g = 0; g < kNG; ++g) load_w(ring[p][g], pw[g], p_c, q);
     p_advance();
   }
 
-  // Items (and their 16-token passes) in order; nchunk is a multiple of P + 1,
-  // so every pass starts at ring slot 0 and the prefetch cursor, P chunks
-  // ahead, crosses into the next pass without a pause.
+  // Items (and their 16-token passes) in order; nchunk is a multiple of 4,
+  // so every pass starts at ring slot 0 and quad boundary, and the prefetch
+  // cursor, P chunks ahead, crosses into the next pass without a pause.
   for (int it = it0; it < it1; ++it) {
     const int a = it / per, i0 = (it - a * per) * 16;
     const int beg = __builtin_amdgcn_readfirstlane(l_off[a]);
@@ -153,17 +191,28 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
       const int xrow = l_tok[beg + (has ? j : 0)];
       f32x4 acc[kNG] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       for (int c = 0; c < nchunk; c += P + 1) {
+        uint32_t sx[kNG], sy[kNG];
+#pragma unroll
+        for (int g = 0; g < kNG; ++g) scale_quad(sraw[g], sx[g], sy[g]);
 #pragma unroll
         for (int u = 0; u <= P; ++u) {
           const int cc = c + u;
 #pragma unroll
-          for (int g = 0; g < kNG; ++g)
-            load_a(ring[(u + P) % (P + 1)][g], pw[g], ps[g], p_c, q, nblk);
+          for (int g = 0; g < kNG; ++g) load_w(ring[(u + P) % (P + 1)][g], pw[g], p_c, q);
           p_advance();
-          const bool ok = cc * kChunkBlocks + 2 * q < nblk;
+          if (u == 0) {
+            // the cursor now stands at the first chunk of the next quad
+#pragma unroll
+            for (int g = 0; g < kNG; ++g)
+              sraw[g] = *reinterpret_cast<const uint2*>(ps[g] + 8 * (p_c + q));
+          }
           float sc[kNG][2];
 #pragma unroll
-          for (int g = 0; g < kNG; ++g) chunk_scales(ring[u][g], ok, sc[g][0], sc[g][1]);
+          for (int g = 0; g < kNG; ++g) {
+            const uint32_t pair = ((u & 1) ? sy[g] : sx[g]) >> ((u & 2) ? 16 : 0);
+            sc[g][0] = e8m0_to_f32(pair & 0xffu);
+            sc[g][1] = e8m0_to_f32((pair >> 8) & 0xffu);
+          }
           const int e0 = cc * kChunkElems + 64 * q;
 #pragma unroll
           for (int m = 0; m < 8; ++m) {
@@ -202,8 +251,12 @@ hipError_t launch_p(const uint8_t* w13, const uint8_t* s13, int cap, const moe_s
 
 }  // namespace
 
-bool ffn_use_resident(int T, int k, int H, int cap, int on_host) {
-  return !on_host && T >= 1 && T <= 16 && resident_lds_bytes(T, k, H, cap) <= kResidentMaxLds;
+bool ffn_use_resident(int T, int k, int H, int cap, int on_host, const void* s13) {
+  // H a multiple of 1024: whole 4-chunk quads per row, 8-byte scale loads
+  // inside the row; the scale tensor 8-byte aligned for those loads.
+  return !on_host && T >= 1 && T <= 16 && H % 1024 == 0 &&
+         (reinterpret_cast<uintptr_t>(s13) & 7u) == 0 &&
+         resident_lds_bytes(T, k, H, cap) <= kResidentMaxLds;
 }
 
 hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int cap,
@@ -216,12 +269,7 @@ hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int c
     (void)hipGetLastError();
     cus = 256;
   }
-  // The deepest ring whose length divides the chunk count.
-  const int nchunk = (H + kChunkElems - 1) / kChunkElems;
-  if (nchunk % 4 == 0) return launch_p<3>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, cus);
-  if (nchunk % 3 == 0) return launch_p<2>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, cus);
-  if (nchunk % 2 == 0) return launch_p<1>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, cus);
-  return launch_p<0>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, cus);
+  return launch_p<3>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, cus);
 }
 
 }  // namespace moe

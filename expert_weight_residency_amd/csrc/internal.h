@@ -50,9 +50,10 @@ hipError_t launch_down_tiled(const uint8_t* w2, const uint8_t* s2, int cap, int 
                              const uint16_t* h_ws, uint16_t* Y, hipStream_t stream);
 
 // Gate/up with every token row resident in LDS (ffn_resident.hip): device
-// banks, 1 <= T <= 16, activations and tables within kResidentMaxLds bytes.
+// banks, 1 <= T <= 16, H a multiple of 1024, an 8-byte aligned scale tensor,
+// activations and tables within kResidentMaxLds bytes.
 constexpr size_t kResidentMaxLds = 144 * 1024;
-bool ffn_use_resident(int T, int k, int H, int cap, int on_host);
+bool ffn_use_resident(int T, int k, int H, int cap, int on_host, const void* s13);
 hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int cap,
                                    const moe_split& split, const uint16_t* x, int T, int k, int H,
                                    int I, uint16_t* h_ws, hipStream_t stream);
