@@ -292,14 +292,13 @@ def main():
     value = float(np.mean(bytes_step) / (ms_per_step / 1e3) / 1e9)
     cold_link = float(np.sum(cold_bytes) / max(c_ms.sum() / 1e3, 1e-12) / 1e9)
 
-    # HBM traffic of the gate/up kernel from committed rocprofv3 counter runs
+    # HBM traffic of the gate/up kernel from committed rocprofv3 counter runs,
+    # used only while the kernel's sources are the ones the counters were taken on
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "traffic_gate_up_full_layer_decode_t16.json")
-    src = os.path.join(ROOT, "expert_weight_residency_amd", "csrc", "ffn_mxfp4.hip")
     if os.path.exists(tpath):
         rec = json.load(open(tpath))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("source_sha256") == sha:
+        if rec.get("source_sha256") == sources_sha256(rec.get("sources", [])):
             traffic = rec.get("bytes_per_launch")
 
     result = {
@@ -334,7 +333,7 @@ def main():
                     "cold_share_of_picks": round(cold_picks / (K * T * k), 4)},
         "swaps_applied": swaps, "swaps_stale": stale,
         "ceilings": ceilings,
-        "roofline": {"kernel": "ffn_gate_up (hot bank)", "bound": "hbm",
+        "roofline": {"kernel": "ffn_gate_up_resident (hot bank)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
     }
@@ -343,6 +342,17 @@ def main():
         result["cpu_baseline"] = cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E,
                                               b13 + b2, account, log)
     print(json.dumps(result), flush=True)
+
+
+def sources_sha256(rel_paths):
+    """sha256 over the named source files, in order (None if any is missing)."""
+    h = hashlib.sha256()
+    for rel in rel_paths:
+        path = os.path.join(ROOT, rel)
+        if not os.path.exists(path):
+            return None
+        h.update(open(path, "rb").read())
+    return h.hexdigest() if rel_paths else None
 
 
 def make_layer_banks(torch, moe, synth, E, n_cold, H, I, Lr, seed, map_kind="fitted"):

@@ -13,8 +13,8 @@
 //    their weight chunks back to back, kP chunks ahead in a register ring, so
 //    the prefetch runs straight across item boundaries. Inside the loop the
 //    only global loads are the weight chunks, issued unconditionally (past
-//    the wavefront's last item it re-reads that item's rows), so waiting for
-//    one chunk never waits for a newer one.
+//    the wavefront's last chunk it re-reads its last 4 chunks, still in
+//    cache), so waiting for one chunk never waits for a newer one.
 //  - Exactly as many wavefronts run as make every run the same length
 //    (ceil(items / ceil(items / wavefronts))), so no wavefront has an extra
 //    item at the end; the idle ones are spread over the workgroups.
@@ -150,13 +150,19 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
   p_rows(p_it);
   auto p_advance = [&]() {
     if (++p_c < nchunk) return;
-    p_c = 0;
-    if (++p_pass < p_npass) return;
-    p_pass = 0;
-    if (p_it + 1 < it1) {
+    if (p_pass + 1 < p_npass) {  // next 16 tokens of the same item: its weights again
+      p_c = 0;
+      ++p_pass;
+    } else if (p_it + 1 < it1) {
+      p_c = 0;
+      p_pass = 0;
       ++p_it;
       p_rows(p_it);
       p_npass = passes_of(p_it);
+    } else {
+      // Past the wavefront's last chunk the loads only keep the stream
+      // unconditional: cycle through the last quad, which is still cached.
+      p_c = nchunk - 4;
     }
   };
 
