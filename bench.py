@@ -10,8 +10,9 @@ decode histogram. Steps rotate through --layers distinct layer banks and use
 fresh routing and activations each step, so the 256 MB Infinity Cache cannot
 hold a step's expert bytes.
 
-One step = moe_route_split (usage counter on) -> hot expert FFN (gate/up, down)
-on the main stream, cold expert FFN on a second stream -> moe_finalize; every
+One step = moe_route_split (usage counter on) -> cold expert FFN on a second
+stream (enqueued first, so its few workgroups start at once) and hot expert FFN
+(gate/up, down) on the main stream -> moe_finalize; every
 64 steps the counter table is snapshotted (moe_usage_counts) at a drained
 barrier, the adaptive policy runs with the pages' defaults, and the swaps it
 proposes are applied with moe_swap_rows before the next step. All inputs are
@@ -41,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer µs/decode step + achieved HBM GB/s (384e top-6 MXFP4, 1 GPU)"
 PEAK_HBM_GBPS = 8000.0
+COLD_BANK = {"inplace": "pinned_host_in_place", "staged": "pinned_host_staged_to_hbm"}
 NOMINAL_LINK_GBPS = 63.0
 
 
@@ -57,6 +59,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
     ap.add_argument("--seed", type=int, default=20260917)
+    ap.add_argument("--cold-path", default="staged", choices=["staged", "inplace"],
+                    help="staged: copy the step's active cold rows into HBM with one contiguous "
+                         "stream each (moe_stage_rows), then run the cold FFN from HBM; inplace: "
+                         "the cold FFN reads the pinned host bank directly")
     ap.add_argument("--workload", default="decode", choices=["decode", "prefill"],
                     help="decode: the default line; prefill: one 4096-token chunk per step "
                          "(counter off), reported with the hot bank's MFMA utilisation")
@@ -135,7 +141,7 @@ def main():
 
     import expert_weight_residency_amd as moe
     import synth
-    from expert_weight_residency_amd.layer import LayerBuffers
+    from expert_weight_residency_amd.layer import ColdStage, LayerBuffers
     from expert_weight_residency_amd.policy import AdaptivePolicy
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -189,6 +195,7 @@ def main():
     w_d = torch.from_numpy(w_np).cuda()
     x_d = torch.from_numpy(x_np.view(np.int16)).cuda()
     bufs = LayerBuffers.allocate(T, k, H, I, n_hot, n_cold)
+    stage = ColdStage(min(n_cold, T * k), H, I) if args.cold_path == "staged" else None
     main_s = torch.cuda.Stream()
     cold_s = main_s if args.serial else torch.cuda.Stream()
     policy = AdaptivePolicy(Lr, E)
@@ -210,12 +217,32 @@ def main():
         split = T * k * 4 + E * 4 + (T * k * 4) * 2
         return gu, gu + dn + cold_act + fin + split, uc * (b13 + b2), uh, uc, pc
 
+    def cold_ffn(s, l, timed):
+        if timed:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(cold_s)
+            ev["c0"].append(e)
+        if stage is None:
+            moe.moe_expert_ffn_mxfp4(cold[l], bufs.cold_split, x_d[s], k, I, bufs.workspace,
+                                     bufs.Y, stream=cold_s)
+        else:
+            staged = moe.moe_stage_rows(cold[l], bufs.cold_split, T, k, stage.bank, stage.rows,
+                                        H, I, stream=cold_s)
+            moe.moe_expert_ffn_mxfp4(stage.bank, staged, x_d[s], k, I, bufs.workspace, bufs.Y,
+                                     stream=cold_s)
+        if timed:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(cold_s)
+            ev["c1"].append(e)
+
     def step(s, timed):
         l = s % Lr
         moe.moe_route_split(ids_d[s], maps_dev[l], n_hot, n_cold, bufs.hot_split, bufs.cold_split,
                             bufs.n_invalid, counts[l], 256, stream=main_s)
         if cold_s is not main_s:
+            # cold bank first on its own stream: its 8 workgroups start beside the hot bank's
             cold_s.wait_stream(main_s)
+            cold_ffn(s, l, timed)
         if timed:
             e = torch.cuda.Event(enable_timing=True)
             e.record(main_s)
@@ -232,16 +259,9 @@ def main():
             e = torch.cuda.Event(enable_timing=True)
             e.record(main_s)
             ev["dn1"].append(e)
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(cold_s)
-            ev["c0"].append(e)
-        moe.moe_expert_ffn_mxfp4(cold[l], bufs.cold_split, x_d[s], k, I, bufs.workspace, bufs.Y,
-                                 stream=cold_s)
-        if timed:
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(cold_s)
-            ev["c1"].append(e)
-        if cold_s is not main_s:
+        if cold_s is main_s:
+            cold_ffn(s, l, timed)
+        else:
             main_s.wait_stream(cold_s)
         moe.moe_finalize(bufs.Y, w_d[s], bufs.out, stream=main_s)
 
@@ -316,7 +336,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"full_layer_decode_t{T}", "experts": E, "top_k": k, "hidden": H,
                    "intermediate": I, "tokens": T, "hot_rows": n_hot, "cold_rows": n_cold,
-                   "weights": "mxfp4", "cold_bank": "pinned_host_in_place", "map": args.map,
+                   "weights": "mxfp4", "cold_bank": COLD_BANK[args.cold_path], "map": args.map,
                    "layer_banks_rotated": Lr, "cold_stream": not args.serial,
                    "policy": not args.no_policy},
         "us_per_layer": round(ms_per_step * 1e3, 1),
@@ -384,7 +404,7 @@ def run_prefill(args):
 
     import expert_weight_residency_amd as moe
     import synth
-    from expert_weight_residency_amd.layer import LayerBuffers
+    from expert_weight_residency_amd.layer import ColdStage, LayerBuffers
 
     E, k, H, I, T = 384, 6, 4096, 2880, 4096
     n_cold = 89
@@ -406,6 +426,7 @@ def run_prefill(args):
     ids_d = torch.from_numpy(ids_np).cuda()
     w_d = torch.from_numpy(w_np).cuda()
     bufs = LayerBuffers.allocate(T, k, H, I, n_hot, n_cold)
+    stage = ColdStage(min(n_cold, T * k), H, I) if args.cold_path == "staged" else None
     main_s = torch.cuda.Stream()
     cold_s = main_s if args.serial else torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -435,8 +456,14 @@ def run_prefill(args):
         if timed:
             rec("dn1", main_s)
             rec("c0", cold_s)
-        moe.moe_expert_ffn_mxfp4(cold[l], bufs.cold_split, x_d[s], k, I, bufs.workspace, bufs.Y,
-                                 stream=cold_s)
+        if stage is None:
+            moe.moe_expert_ffn_mxfp4(cold[l], bufs.cold_split, x_d[s], k, I, bufs.workspace,
+                                     bufs.Y, stream=cold_s)
+        else:
+            staged = moe.moe_stage_rows(cold[l], bufs.cold_split, T, k, stage.bank, stage.rows,
+                                        H, I, stream=cold_s)
+            moe.moe_expert_ffn_mxfp4(stage.bank, staged, x_d[s], k, I, bufs.workspace, bufs.Y,
+                                     stream=cold_s)
         if timed:
             rec("c1", cold_s)
         if cold_s is not main_s:
@@ -484,7 +511,7 @@ def run_prefill(args):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"full_layer_prefill_t{T}", "experts": E, "top_k": k,
                    "hidden": H, "intermediate": I, "tokens": T, "hot_rows": n_hot,
-                   "cold_rows": n_cold, "weights": "mxfp4", "cold_bank": "pinned_host_in_place",
+                   "cold_rows": n_cold, "weights": "mxfp4", "cold_bank": COLD_BANK[args.cold_path],
                    "map": args.map, "layer_banks_rotated": Lr, "counter": False,
                    "cold_stream": not args.serial},
         "us_per_layer": round(ms * 1e3, 1),

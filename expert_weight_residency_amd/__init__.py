@@ -22,7 +22,8 @@ MOE_MAX_TOPK = 32
 # entry points declared in include/moe_residency.h
 ENTRY_POINTS = ("moe_expert_bytes", "moe_ffn_workspace_bytes", "moe_route_split",
                 "moe_expert_ffn_mxfp4", "moe_expert_gate_up_mxfp4", "moe_expert_down_mxfp4",
-                "moe_finalize", "moe_usage_counts", "moe_swap_rows", "moe_last_error")
+                "moe_stage_rows", "moe_finalize", "moe_usage_counts", "moe_swap_rows",
+                "moe_last_error")
 
 
 class MoeError(RuntimeError):
@@ -75,6 +76,9 @@ def lib():
         L.moe_expert_down_mxfp4.restype = i32
         L.moe_expert_down_mxfp4.argtypes = [ctypes.POINTER(MoeBankC), MoeSplitC, i32, i32, i32, i32,
                                             vp, vp, vp]
+        L.moe_stage_rows.restype = i32
+        L.moe_stage_rows.argtypes = [ctypes.POINTER(MoeBankC), MoeSplitC, i32, i32,
+                                     ctypes.POINTER(MoeBankC), vp, i32, i32, vp]
         L.moe_finalize.restype = i32
         L.moe_finalize.argtypes = [vp, vp, i32, i32, i32, vp, vp]
         L.moe_usage_counts.restype = i32
@@ -199,6 +203,16 @@ def moe_expert_down_mxfp4(bank: Bank, split: Split, T: int, k: int, H: int, I: i
     b = bank.abi()
     _check(lib().moe_expert_down_mxfp4(ctypes.byref(b), split.abi(), T, k, H, I,
                                        workspace.data_ptr(), Y.data_ptr(), _stream(stream)))
+
+
+def moe_stage_rows(src: Bank, split: Split, T: int, k: int, dst: Bank, dst_rows, H: int, I: int,
+                   stream=None) -> Split:
+    """Copy src's active rows (per split) to rows 0.. of the device bank dst;
+    returns the split that drives the expert FFN on dst."""
+    s, d = src.abi(), dst.abi()
+    _check(lib().moe_stage_rows(ctypes.byref(s), split.abi(), T, k, ctypes.byref(d),
+                                dst_rows.data_ptr(), H, I, _stream(stream)))
+    return Split(split.n_active, dst_rows, split.row_off, split.slots)
 
 
 def moe_finalize(Y, topk_w, out, stream=None) -> None:

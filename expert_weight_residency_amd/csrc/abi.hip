@@ -177,6 +177,40 @@ int moe_expert_ffn_mxfp4(const moe_bank* bank, moe_split split, const uint16_t* 
   return ok();
 }
 
+int moe_stage_rows(const moe_bank* src, moe_split split, int T, int k, const moe_bank* dst,
+                   int32_t* dst_rows, int H, int I, void* stream) {
+  int rc;
+  if (T < 0) return fail(MOE_EINVAL, "T=%d must be >= 0", T);
+  if (k < 1 || k > MOE_MAX_TOPK) return fail(MOE_EINVAL, "k=%d outside [1, %d]", k, MOE_MAX_TOPK);
+  if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_EINVAL, "T*k too large");
+  if (H <= 0 || H % 64 || I <= 0 || I % 64) return fail(MOE_EINVAL, "H, I must be multiples of 64");
+  if (!src || !dst) return fail(MOE_EINVAL, "src and dst must not be NULL");
+  if (src->n_rows < 0 || src->n_rows > MOE_MAX_ROWS)
+    return fail(MOE_EINVAL, "src rows %d outside [0, %d]", src->n_rows, MOE_MAX_ROWS);
+  if (T == 0 || src->n_rows == 0) return ok();
+  if ((rc = check_split(split, "src"))) return rc;
+  if (!dst_rows) return fail(MOE_EINVAL, "dst_rows must not be NULL");
+  if (dst->on_host) return fail(MOE_EINVAL, "dst must be a device bank (on_host = 0)");
+  const int64_t picks = (int64_t)T * k;
+  const int cap = (int)(src->n_rows < picks ? src->n_rows : picks);
+  if (dst->n_rows < cap)
+    return fail(MOE_EINVAL, "dst holds %d rows, the split can name %d", dst->n_rows, cap);
+  const uint8_t* sp[4];
+  const uint8_t* dq[4];
+  if ((rc = bank_device_ptrs(src, sp)) || (rc = bank_device_ptrs(dst, dq))) return rc;
+  const uint64_t rb[4] = {(uint64_t)2 * I * (H / 2), (uint64_t)2 * I * (H / 32),
+                          (uint64_t)H * (I / 2), (uint64_t)H * (I / 32)};
+  for (int t = 0; t < 4; ++t)
+    if ((reinterpret_cast<uintptr_t>(sp[t]) | reinterpret_cast<uintptr_t>(dq[t])) & 15u)
+      return fail(MOE_EINVAL, "bank tensor %d must be 16-byte aligned for staging", t);
+  uint8_t* dp[4] = {const_cast<uint8_t*>(dq[0]), const_cast<uint8_t*>(dq[1]),
+                    const_cast<uint8_t*>(dq[2]), const_cast<uint8_t*>(dq[3])};
+  hipError_t e = moe::launch_stage_rows(sp, dp, rb, split, dst_rows,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_EHIP, "stage rows launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int moe_finalize(const uint16_t* Y, const float* topk_w, int T, int k, int H, uint16_t* out,
                  void* stream) {
   if (T < 0) return fail(MOE_EINVAL, "T=%d must be >= 0", T);

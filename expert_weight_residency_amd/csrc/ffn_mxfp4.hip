@@ -62,6 +62,7 @@ constexpr int kNG = 2;            // 16-row MFMA groups per wavefront
 // kernel keeps ~95% of its speed. (Spreading the same wavefronts over 32 CUs
 // reads the link slightly faster but slows the hot bank 2.5x.)
 constexpr int kHostReadWaves = 64;
+static_assert(kHostReadWaves / kWavesHost == kHostBankCUs, "host-bank launch width");
 
 // Stage rows src_row(n) for n < nvalid into the LDS tile, zero past K.
 template <typename RowFn>
@@ -248,8 +249,8 @@ int ffn_max_reduction() { return kLdsTile / (int)sizeof(uint16_t); }
 hipError_t launch_gate_up(const uint8_t* w13, const uint8_t* s13, int cap, int on_host,
                           const moe_split& sp, const uint16_t* x, int T, int k, int H, int I,
                           uint16_t* h_ws, hipStream_t stream) {
-  if (ffn_use_resident(T, k, H, cap, on_host, s13))
-    return launch_gate_up_resident(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream);
+  if (ffn_use_resident(T, k, H, cap, s13))
+    return launch_gate_up_resident(w13, s13, cap, on_host, sp, x, T, k, H, I, h_ws, stream);
   if (ffn_use_tiled(T, k, cap))
     return launch_gate_up_tiled(w13, s13, cap, on_host, sp, x, T, k, H, I, h_ws, stream);
   const int w = on_host ? kWavesHost : kWavesDevice;

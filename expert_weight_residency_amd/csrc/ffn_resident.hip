@@ -4,7 +4,10 @@
 // the routed MXFP4 expert FFN per bank), organised so that a wavefront's
 // weight stream never drains:
 //
-//  - One workgroup of 16 wavefronts per CU. It stages every token row of x
+//  - One workgroup of 16 wavefronts per CU: for a device bank on all CUs but
+//    the few a host-bank launch beside it holds; for a bank in host memory on
+//    those few (its wavefronts keep enough reads in flight to fill the link).
+//    It stages every token row of x
 //    (T <= 16 rows of H) and the split's bookkeeping (active rows, offsets,
 //    the token of every slot) into LDS once, behind one barrier. After that
 //    no wavefront waits for another.
@@ -257,15 +260,15 @@ hipError_t launch_p(const uint8_t* w13, const uint8_t* s13, int cap, const moe_s
 
 }  // namespace
 
-bool ffn_use_resident(int T, int k, int H, int cap, int on_host, const void* s13) {
+bool ffn_use_resident(int T, int k, int H, int cap, const void* s13) {
   // H a multiple of 1024: whole 4-chunk quads per row, 8-byte scale loads
   // inside the row; the scale tensor 8-byte aligned for those loads.
-  return !on_host && T >= 1 && T <= 16 && H % 1024 == 0 &&
+  return T >= 1 && T <= 16 && H % 1024 == 0 &&
          (reinterpret_cast<uintptr_t>(s13) & 7u) == 0 &&
          resident_lds_bytes(T, k, H, cap) <= kResidentMaxLds;
 }
 
-hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int cap,
+hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int cap, int on_host,
                                    const moe_split& sp, const uint16_t* x, int T, int k, int H,
                                    int I, uint16_t* h_ws, hipStream_t stream) {
   int dev = 0, cus = 0;
@@ -275,7 +278,11 @@ hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int c
     (void)hipGetLastError();
     cus = 256;
   }
-  return launch_p<3>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, cus);
+  // A bank in host memory runs on kHostBankCUs workgroups (16 wavefronts,
+  // 3 chunks each in flight: enough to fill the host link); a device bank on
+  // the other CUs.
+  const int grid = on_host ? kHostBankCUs : (cus > 2 * kHostBankCUs ? cus - kHostBankCUs : cus);
+  return launch_p<3>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, grid);
 }
 
 }  // namespace moe

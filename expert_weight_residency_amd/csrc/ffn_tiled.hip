@@ -327,6 +327,7 @@ unsigned tiled_grid(int cap, int T, int k, int blocks, int on_host) {
   const long long max_tiles = (long long)T * k / kTok + cap;
   const long long max_items = max_tiles * blocks;
   const int host_wgs = kTiledHostWaves / kWaves;
+  static_assert(kTiledHostWaves / kWaves == kHostBankCUs, "host-bank launch width");
   long long g = on_host ? host_wgs : device_cus() - host_wgs;
   if (g > max_items) g = max_items;
   return (unsigned)(g < 1 ? 1 : g);

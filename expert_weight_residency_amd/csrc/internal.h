@@ -49,12 +49,17 @@ hipError_t launch_down_tiled(const uint8_t* w2, const uint8_t* s2, int cap, int 
                              const moe_split& split, int T, int k, int H, int I,
                              const uint16_t* h_ws, uint16_t* Y, hipStream_t stream);
 
-// Gate/up with every token row resident in LDS (ffn_resident.hip): device
-// banks, 1 <= T <= 16, H a multiple of 1024, an 8-byte aligned scale tensor,
-// activations and tables within kResidentMaxLds bytes.
+// CUs a host-resident bank's FFN launch occupies (each of its workgroups fills
+// a CU). Persistent device-bank launches leave them free, so a cold-bank launch
+// running beside them never holds a device-bank workgroup back.
+constexpr int kHostBankCUs = 8;
+
+// Gate/up with every token row resident in LDS (ffn_resident.hip): 1 <= T <=
+// 16, H a multiple of 1024, an 8-byte aligned scale tensor, activations and
+// tables within kResidentMaxLds bytes; either bank.
 constexpr size_t kResidentMaxLds = 144 * 1024;
-bool ffn_use_resident(int T, int k, int H, int cap, int on_host, const void* s13);
-hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int cap,
+bool ffn_use_resident(int T, int k, int H, int cap, const void* s13);
+hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int cap, int on_host,
                                    const moe_split& split, const uint16_t* x, int T, int k, int H,
                                    int I, uint16_t* h_ws, hipStream_t stream);
 
@@ -63,6 +68,12 @@ constexpr int kTiledMinPicksPerRow = 16;
 // Wavefronts that read a host-resident bank at once in the token-tiled kernels.
 constexpr int kTiledHostWaves = 64;
 bool ffn_use_tiled(int T, int k, int cap);
+
+// Copy split.active_rows[a] of the four src tensors to row a of dst, and
+// dst_rows[a] = a, for a < *split.n_active (stage_rows.hip).
+hipError_t launch_stage_rows(const uint8_t* const src[4], uint8_t* const dst[4],
+                             const uint64_t row_bytes[4], const moe_split& split,
+                             int32_t* dst_rows, hipStream_t stream);
 
 hipError_t launch_finalize(const uint16_t* Y, const float* w, int T, int k, int H, uint16_t* out,
                            hipStream_t stream);

@@ -168,6 +168,30 @@ int moe_expert_down_mxfp4(const moe_bank *bank, moe_split split, int T, int k, i
                           const void *workspace, uint16_t *Y, void *stream);
 
 /*
+ * moe_stage_rows -- copy one bank's active rows into a compact device bank.
+ *
+ * For a = 0 .. n_active-1 (n_active = *split.n_active on the device): row
+ * split.active_rows[a] of each of the four tensors of `src` is copied to row a
+ * of `dst`, and dst_rows[a] = a. The split {split.n_active, dst_rows,
+ * split.row_off, split.slots} then drives moe_expert_ffn_mxfp4 on `dst` with
+ * results identical to `split` on `src` (the FFN arithmetic does not depend on
+ * the bank). For a cold bank in pinned host memory this replaces the FFN's
+ * row-interleaved reads over the host link with one contiguous stream per
+ * touched expert, copied into HBM before use ("Should a GB300 Prefetch Its
+ * Cold Experts?": bring a cold expert into HBM instead of reading it in place;
+ * "We Built the Counter", section 6: cold reads in place as the baseline).
+ *
+ * src: the bank the split was made for (host or device). split: its
+ * moe_route_split output for a step of T tokens, k picks each. dst: a device
+ * bank (on_host = 0) with n_rows >= min(src->n_rows, T*k); rows past n_active
+ * are left unwritten. dst_rows: device int32 [min(src->n_rows, T*k)]. All
+ * tensors 16-byte aligned. Launches one kernel; nothing when T == 0 or src has
+ * no rows.
+ */
+int moe_stage_rows(const moe_bank *src, moe_split split, int T, int k, const moe_bank *dst,
+                   int32_t *dst_rows, int H, int I, void *stream);
+
+/*
  * moe_finalize -- ordered fp32 FMA combine of the k rows of each token.
  *
  * out[t][o] = bf16_rne(acc) with acc = +0.0f and, for j = 0 .. k-1 in the

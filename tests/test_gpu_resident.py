@@ -7,8 +7,8 @@ families for every pick:
   - decode shapes (T = 1, 7, 16 at full H = 4096, I = 2880; a ragged I);
   - an expert picked by all 16 tokens (one full 16-token pass) and an expert
     with 64 slots from duplicate ids (four passes);
-  - bitwise against the host-bank path (the decode kernel: a cold bank in
-    pinned memory never uses this kernel) and the token-tiled path.
+  - bitwise against the decode kernel (steps with T > 16), with the bank in
+    HBM and in pinned host memory; a pinned-memory bank against the oracle.
 """
 import numpy as np
 import pytest
@@ -83,17 +83,32 @@ def test_resident_full_pass_and_duplicates():
     _check(rm, hot, cold, ids_dup, np.full((T, k), 0.25, np.float32), x, H, I)
 
 
-@pytest.mark.parametrize("T", [4, 16])
-def test_resident_equals_host_bank_path_bitwise(T):
-    """Every expert once in HBM (resident kernel) and once in pinned host
-    memory (decode kernel): identical Y rows."""
-    E, k, H, I = 16, 2, 4096, 2880
+@pytest.mark.parametrize("where", ["device", "pinned_host"])
+def test_resident_equals_decode_kernel_bitwise(where):
+    """The first 4 tokens of a 20-token step (T > 16: decode kernel) and the
+    same 4 tokens alone (resident kernel) give identical Y rows, with every
+    expert in HBM or every expert in pinned host memory."""
+    E, k, H, I, T = 16, 2, 4096, 2880, 20
     all_map, owners, _ = synth.all_hot_map(E)
     arrays = host_bank(owners, 13, 0, H, I)
     ids, w = synth.gaussian_routing(T, k, E, 13)
     x = synth.activations(T, H, 13)
-    Yd, _, _ = run_layer(device_bank(arrays), None, all_map, ids, w, x, H, I)
-    cold_map = -1 - all_map  # every expert cold, same rows
-    empty = host_bank(np.zeros(0, np.int32), 13, 0, H, I)
-    Yh, _, _ = run_layer(device_bank(empty), pinned_bank(arrays), cold_map, ids, w, x, H, I)
-    assert np.array_equal(Yd, Yh)
+    if where == "device":
+        bank, rm, other = device_bank(arrays), all_map, None
+        run = lambda n: run_layer(bank, other, rm, ids[:n], w[:n], x[:n], H, I)[0]
+    else:
+        empty = device_bank(host_bank(np.zeros(0, np.int32), 13, 0, H, I))
+        bank, rm = pinned_bank(arrays), -1 - all_map  # every expert cold, same rows
+        run = lambda n: run_layer(empty, bank, rm, ids[:n], w[:n], x[:n], H, I)[0]
+    Y20, Y4 = run(T), run(4)
+    assert np.array_equal(Y20[: 4 * k], Y4)
+
+
+def test_resident_host_bank_matches_oracle():
+    """Resident kernel reading a bank in pinned host memory, against the oracle."""
+    E, k, H, I, T = 32, 6, 4096, 2880, 16
+    rm, ho, co = synth.random_map(E, 8, 17)
+    hot, cold = host_bank(ho, 17, 0, H, I), host_bank(co, 17, 0, H, I)
+    ids, w = synth.skewed_routing(T, k, E, 17, 0, 0)
+    x = synth.activations(T, H, 17)
+    _check(rm, hot, cold, ids, w, x, H, I, cold_pinned=True)

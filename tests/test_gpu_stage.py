@@ -1,0 +1,100 @@
+"""GPU tests of moe_stage_rows: the cold bank's active rows copied into a
+compact HBM bank before the cold FFN.
+
+Bit-exact: the staged rows equal the source rows the split names, the staged
+row list is 0..n_active-1, and a layer run through the stage gives the same Y
+rows and output as the in-place run (small shape, and the full shape with the
+fitted map and 16 decode tokens), including a step with no cold picks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import expert_weight_residency_amd as moe
+import synth
+from expert_weight_residency_amd.layer import ColdStage, LayerBuffers, ResidencyLayer
+from gpu_util import device_bank, host_bank, pinned_bank, routing_tensors
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.lib()
+    yield
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def _run(hot, cold, rm, ids, w, x, H, I, stage, cold_stream=None):
+    T, k = ids.shape
+    ids_d, w_d, x_d = routing_tensors(ids, w, x)
+    bufs = LayerBuffers.allocate(T, k, H, I, hot.n_rows, cold.n_rows)
+    layer = ResidencyLayer(hot, cold, torch.from_numpy(rm).cuda(), H, I, stage=stage)
+    layer.forward(x_d, ids_d, w_d, bufs, cold_stream=cold_stream)
+    torch.cuda.synchronize()
+    return (bufs.Y[: T * k].cpu().numpy().copy(), bufs.out[:T].cpu().numpy().copy(), bufs)
+
+
+def test_stage_copies_named_rows():
+    E, k, H, I, T = 24, 3, 512, 320, 12
+    rm, ho, co = synth.random_map(E, 9, 3)
+    cold_arr = host_bank(co, 3, 0, H, I)
+    cold = pinned_bank(cold_arr)
+    ids, _ = synth.skewed_routing(T, k, E, 3, 0, 0)
+    hs, cs = moe.Split.empty(E - 9, T, k), moe.Split.empty(9, T, k)
+    ninv = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.moe_route_split(torch.from_numpy(ids).cuda(), torch.from_numpy(rm).cuda(), E - 9, 9, hs, cs,
+                        ninv)
+    stage = ColdStage(min(9, T * k), H, I)
+    stage.rows.fill_(-5)
+    staged = moe.moe_stage_rows(cold, cs, T, k, stage.bank, stage.rows, H, I)
+    torch.cuda.synchronize()
+    active, _, _ = cs.to_host()
+    n = len(active)
+    log(f"{n} active cold rows")
+    assert n > 0
+    assert np.array_equal(staged.active_rows[:n].cpu().numpy(), np.arange(n))
+    for name in ("w13", "s13", "w2", "s2"):
+        got = getattr(stage.bank, name)[:n].cpu().numpy()
+        assert np.array_equal(got, cold_arr[name][active]), name
+
+
+@pytest.mark.parametrize("two_streams", [False, True])
+def test_staged_layer_equals_in_place_bitwise(two_streams):
+    E, k, H, I, T = 32, 4, 1024, 512, 24
+    rm, ho, co = synth.random_map(E, 10, 5)
+    hot = device_bank(host_bank(ho, 5, 0, H, I))
+    cold = pinned_bank(host_bank(co, 5, 0, H, I))
+    ids, w = synth.skewed_routing(T, k, E, 5, 0, 0)
+    x = synth.activations(T, H, 5)
+    cs = torch.cuda.Stream() if two_streams else None
+    Y0, o0, _ = _run(hot, cold, rm, ids, w, x, H, I, None, cs)
+    Y1, o1, _ = _run(hot, cold, rm, ids, w, x, H, I, ColdStage(min(10, T * k), H, I), cs)
+    assert np.array_equal(Y0, Y1) and np.array_equal(o0, o1)
+
+
+def test_staged_full_shape_decode_bitwise():
+    E, k, H, I, T, n_cold = 384, 6, 4096, 2880, 16, 89
+    rm, ho, co = synth.fitted_map(E, n_cold, 7, 0)
+    hb = moe.Bank(*[torch.empty(s, dtype=torch.uint8, device="cuda")
+                    for s in synth.tensor_shapes(len(ho), H, I).values()], on_host=False)
+    synth.fill_bank_device(hb.tensors(), torch.from_numpy(ho).cuda(), 7, 0, H, I)
+    cb = moe.Bank(*[torch.empty(s, dtype=torch.uint8, pin_memory=True)
+                    for s in synth.tensor_shapes(n_cold, H, I).values()], on_host=True)
+    synth.fill_bank_host(cb.tensors(), co, 7, 0, H, I)
+    stage = ColdStage(min(n_cold, T * k), H, I)
+    for step in range(3):
+        ids, w = synth.skewed_routing(T, k, E, 7, 0, step)
+        if step == 2:  # no cold picks at all
+            hot_ids = ho[:E - n_cold]
+            ids = hot_ids[np.arange(T * k).reshape(T, k) % len(hot_ids)].astype(np.int32)
+        x = synth.activations(T, H, 7, 0, step)
+        n_cold_picks = int((rm[ids] < 0).sum())
+        log(f"full shape step {step}: {n_cold_picks} cold picks")
+        Y0, o0, _ = _run(hb, cb, rm, ids, w, x, H, I, None, torch.cuda.Stream())
+        Y1, o1, _ = _run(hb, cb, rm, ids, w, x, H, I, stage, torch.cuda.Stream())
+        assert np.array_equal(Y0, Y1) and np.array_equal(o0, o1)
