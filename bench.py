@@ -63,9 +63,14 @@ def parse():
                     help="staged: copy the step's active cold rows into HBM with one contiguous "
                          "stream each (moe_stage_rows), then run the cold FFN from HBM; inplace: "
                          "the cold FFN reads the pinned host bank directly")
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill"],
-                    help="decode: the default line; prefill: one 4096-token chunk per step "
-                         "(counter off), reported with the hot bank's MFMA utilisation")
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "step40", "highconc", "offdomain"],
+                    help="decode: the default line (one layer of 16 tokens per step); prefill: "
+                         "one 4096-token chunk per step (counter off), with the hot bank's MFMA "
+                         "utilisation; step40: 40 layer calls of 7 tokens per step; highconc: "
+                         "112 tokens per step (--map fitted or positional); offdomain: 7 tokens, "
+                         "map fitted to one ranking, traffic from another, the adaptive policy "
+                         "moving experts, reported in windows")
     return ap.parse_args()
 
 
@@ -148,6 +153,21 @@ def main():
     moe.lib()
     if args.workload == "prefill":
         return run_prefill(args)
+    lps, off_domain, wname = 1, False, None
+    if args.workload == "step40":
+        args.tokens, lps = 7, 40
+        args.steps, args.warmup = min(args.steps, 32), min(args.warmup, 4)
+        wname = "full_step_40_layers_t7"
+    elif args.workload == "highconc":
+        args.tokens = 112
+        args.steps, args.warmup = min(args.steps, 64), min(args.warmup, 8)
+        wname = f"full_layer_decode_t112_{args.map}_map"
+    elif args.workload == "offdomain":
+        # every layer bank runs on every step (as the layers of a model do), so each
+        # bank's counter sees 64 x 7 x 6 picks per policy read
+        args.tokens, off_domain, lps = 7, True, args.layers
+        args.steps, args.warmup = 1536, min(args.warmup, 8)
+        wname = f"off_domain_decode_t7_{args.layers}_layers"
     E, k, H, I, T = 384, 6, 4096, 2880, args.tokens
     n_cold = 89
     n_hot = E - n_cold
@@ -183,14 +203,21 @@ def main():
     log(f"{Lr} layer banks resident: {Lr * n_hot * (b13 + b2) / 2**30:.1f} GiB HBM, "
         f"{Lr * n_cold * (b13 + b2) / 2**30:.1f} GiB pinned host")
 
-    # --- per-step inputs, generated and uploaded before timing ---------------
+    # --- per-call inputs, generated and uploaded before timing ---------------
+    # call c = step * lps + j runs on layer bank c % Lr; its routing follows that
+    # bank's ranking (or, off-domain, an independent ranking of the same shape)
     S = args.warmup + args.steps
-    ids_np = np.empty((S, T, k), np.int32)
-    w_np = np.empty((S, T, k), np.float32)
-    x_np = np.empty((S, T, H), np.uint16)
-    for s in range(S):
-        ids_np[s], w_np[s] = synth.skewed_routing(T, k, E, seed, s % Lr, s)
-        x_np[s] = synth.activations(T, H, seed, s % Lr, s)
+    C = S * lps
+    perms = [synth.layer_permutation(E, seed ^ 0x0FFD0 if off_domain else seed, l)
+             for l in range(Lr)]
+    ids_np = np.empty((C, T, k), np.int32)
+    w_np = np.empty((C, T, k), np.float32)
+    NX = min(C, 64)
+    x_np = np.empty((NX, T, H), np.uint16)
+    for c in range(C):
+        ids_np[c], w_np[c] = synth.skewed_routing(T, k, E, seed, c % Lr, c, perm=perms[c % Lr])
+    for c in range(NX):
+        x_np[c] = synth.activations(T, H, seed, c % Lr, c)
     ids_d = torch.from_numpy(ids_np).cuda()
     w_d = torch.from_numpy(w_np).cuda()
     x_d = torch.from_numpy(x_np.view(np.int16)).cuda()
@@ -204,8 +231,8 @@ def main():
     ev = {name: [] for name in ("gu0", "gu1", "dn1", "c0", "c1")}
     bytes_step, hot_bytes_gu, cold_bytes, uh_list, uc_list, cold_picks = [], [], [], [], [], 0
 
-    def account(s, rm):
-        ids = ids_np[s]
+    def account(c, rm):
+        ids = ids_np[c]
         m = rm[ids]
         hot_ids, cold_ids = ids[m >= 0], ids[m < 0]
         uh, uc = len(np.unique(hot_ids)), len(np.unique(cold_ids))
@@ -217,18 +244,19 @@ def main():
         split = T * k * 4 + E * 4 + (T * k * 4) * 2
         return gu, gu + dn + cold_act + fin + split, uc * (b13 + b2), uh, uc, pc
 
-    def cold_ffn(s, l, timed):
+    def cold_ffn(c, l, timed):
+        xc = x_d[c % NX]
         if timed:
             e = torch.cuda.Event(enable_timing=True)
             e.record(cold_s)
             ev["c0"].append(e)
         if stage is None:
-            moe.moe_expert_ffn_mxfp4(cold[l], bufs.cold_split, x_d[s], k, I, bufs.workspace,
+            moe.moe_expert_ffn_mxfp4(cold[l], bufs.cold_split, xc, k, I, bufs.workspace,
                                      bufs.Y, stream=cold_s)
         else:
             staged = moe.moe_stage_rows(cold[l], bufs.cold_split, T, k, stage.bank, stage.rows,
                                         H, I, stream=cold_s)
-            moe.moe_expert_ffn_mxfp4(stage.bank, staged, x_d[s], k, I, bufs.workspace, bufs.Y,
+            moe.moe_expert_ffn_mxfp4(stage.bank, staged, xc, k, I, bufs.workspace, bufs.Y,
                                      stream=cold_s)
         if timed:
             e = torch.cuda.Event(enable_timing=True)
@@ -236,18 +264,23 @@ def main():
             ev["c1"].append(e)
 
     def step(s, timed):
-        l = s % Lr
-        moe.moe_route_split(ids_d[s], maps_dev[l], n_hot, n_cold, bufs.hot_split, bufs.cold_split,
+        for j in range(lps):
+            layer_call(s * lps + j, timed and j == 0)
+
+    def layer_call(c, timed):
+        l = c % Lr
+        xc = x_d[c % NX]
+        moe.moe_route_split(ids_d[c], maps_dev[l], n_hot, n_cold, bufs.hot_split, bufs.cold_split,
                             bufs.n_invalid, counts[l], 256, stream=main_s)
         if cold_s is not main_s:
             # cold bank first on its own stream: its 8 workgroups start beside the hot bank's
             cold_s.wait_stream(main_s)
-            cold_ffn(s, l, timed)
+            cold_ffn(c, l, timed)
         if timed:
             e = torch.cuda.Event(enable_timing=True)
             e.record(main_s)
             ev["gu0"].append(e)
-        moe.moe_expert_gate_up_mxfp4(hot[l], bufs.hot_split, x_d[s], k, I, bufs.workspace,
+        moe.moe_expert_gate_up_mxfp4(hot[l], bufs.hot_split, xc, k, I, bufs.workspace,
                                      stream=main_s)
         if timed:
             e = torch.cuda.Event(enable_timing=True)
@@ -260,10 +293,10 @@ def main():
             e.record(main_s)
             ev["dn1"].append(e)
         if cold_s is main_s:
-            cold_ffn(s, l, timed)
+            cold_ffn(c, l, timed)
         else:
             main_s.wait_stream(cold_s)
-        moe.moe_finalize(bufs.Y, w_d[s], bufs.out, stream=main_s)
+        moe.moe_finalize(bufs.Y, w_d[c], bufs.out, stream=main_s)
 
     def barrier():
         nonlocal swaps, stale
@@ -288,18 +321,36 @@ def main():
             step(s, False)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
+        windows, win_t, win_picks, win_cold, win_swaps = [], t0, 0, 0, 0
         for i in range(args.steps):
             s = args.warmup + i
-            gu, tot, cb, uh, uc, pc = account(s, maps_host[s % Lr])
-            hot_bytes_gu.append(gu)
-            bytes_step.append(tot)
-            cold_bytes.append(cb)
-            uh_list.append(uh)
-            uc_list.append(uc)
-            cold_picks += pc
+            step_bytes = 0
+            for j in range(lps):
+                c = s * lps + j
+                gu, tot, cb, uh, uc, pc = account(c, maps_host[c % Lr])
+                step_bytes += tot
+                if j == 0:
+                    hot_bytes_gu.append(gu)
+                    cold_bytes.append(cb)
+                uh_list.append(uh)
+                uc_list.append(uc)
+                cold_picks += pc
+                win_cold += pc
+                win_picks += T * k
+            bytes_step.append(step_bytes)
             step(s, True)
             if not args.no_policy and (s + 1) % policy.cfg.read_every == 0:
+                before = swaps
                 barrier()
+                win_swaps += swaps - before
+            if off_domain and (i + 1) % 128 == 0:
+                torch.cuda.synchronize()
+                now = time.perf_counter()
+                windows.append({"steps": [i - 127, i + 1],
+                                "cold_share_of_picks": round(win_cold / win_picks, 4),
+                                "us_per_layer": round((now - win_t) * 1e6 / (128 * lps), 1),
+                                "swaps_applied": win_swaps})
+                win_t, win_picks, win_cold, win_swaps = now, 0, 0, 0
         torch.cuda.synchronize()
         t1 = time.perf_counter()
 
@@ -334,12 +385,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"full_layer_decode_t{T}", "experts": E, "top_k": k, "hidden": H,
+        "config": {"workload": wname or f"full_layer_decode_t{T}", "experts": E, "top_k": k,
+                   "hidden": H, "layers_per_step": lps, "traffic": "off-domain" if off_domain
+                   else "in-domain",
                    "intermediate": I, "tokens": T, "hot_rows": n_hot, "cold_rows": n_cold,
                    "weights": "mxfp4", "cold_bank": COLD_BANK[args.cold_path], "map": args.map,
                    "layer_banks_rotated": Lr, "cold_stream": not args.serial,
                    "policy": not args.no_policy},
-        "us_per_layer": round(ms_per_step * 1e3, 1),
+        "us_per_layer": round(ms_per_step * 1e3 / lps, 1),
         "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
         "hot_gate_up_us": round(float(gu_ms.mean() * 1e3), 1),
         "hot_down_us": round(float(dn_ms.mean() * 1e3), 1),
@@ -350,8 +403,9 @@ def main():
                       "nominal_GBps": NOMINAL_LINK_GBPS},
         "routing": {"hot_unique_per_step": round(float(np.mean(uh_list)), 2),
                     "cold_unique_per_step": round(float(np.mean(uc_list)), 2),
-                    "cold_share_of_picks": round(cold_picks / (K * T * k), 4)},
+                    "cold_share_of_picks": round(cold_picks / (K * lps * T * k), 4)},
         "swaps_applied": swaps, "swaps_stale": stale,
+        **({"windows": windows} if off_domain else {}),
         "ceilings": ceilings,
         "roofline": {"kernel": "ffn_gate_up_resident (hot bank)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -360,7 +414,7 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E,
-                                              b13 + b2, account, log)
+                                              b13 + b2, account, log, lps)
     print(json.dumps(result), flush=True)
 
 
@@ -561,23 +615,24 @@ def cpu_baseline_prefill(args, ids, w, layer, H, I, E, gpu_ms, log):
                       "and cold, plus finalize), time scaled by 4096/48"}
 
 
-def cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E, bexp, account, log):
+def cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E, bexp, account, log, lps=1):
     """The oracle on sampled steps of the same workload (whole layer: all picks,
     hot and cold, plus finalize), until about 10 s of CPU time."""
     import oracle
     import synth
     t_tot, b_tot, n = 0.0, 0.0, 0
     for s in range(args.warmup, args.warmup + min(args.steps, 4)):
-        l = s % Lr
-        ids = ids_np[s]
+        c = s * lps  # the step's first layer call
+        l = c % Lr
+        ids = ids_np[c]
         U = np.unique(ids)
         bank = oracle.Bank(**synth.make_bank_host(U, args.seed, l, H, I))
         rm = np.full(E, -(10 ** 6), np.int32)
         rm[U] = np.arange(len(U), dtype=np.int32)
         t0 = time.perf_counter()
-        oracle.moe_layer(bank, None, rm, ids, w_np[s], x_np[s], H, I)
+        oracle.moe_layer(bank, None, rm, ids, w_np[c], x_np[c % len(x_np)], H, I)
         t_tot += time.perf_counter() - t0
-        b_tot += account(s, maps_host[l])[1]
+        b_tot += account(c, maps_host[l])[1]
         n += 1
         if t_tot > 10.0:
             break
