@@ -1,0 +1,320 @@
+// Down GEMM for decode-sized steps as a persistent, continuously streaming
+// kernel (gfx950). Same operation as the down kernels in ffn_mxfp4.hip and
+// ffn_tiled.hip: Y[s][o] = bf16(Wdown[r][o] . h[s]) for every slot s routed to
+// active row r ("vLLM: Pin Hot Experts", section "Results, September 17": the
+// routed MXFP4 expert FFN per bank, unweighted rows for a later finalize).
+//
+//  - One workgroup of 16 wavefronts per CU (for a device bank on all CUs but
+//    the few a host-bank launch beside it holds; for a bank in host memory on
+//    those few). Work item = kNG groups of 16 output rows of one active expert.
+//    Items are ordered (expert, row block); workgroup b takes one contiguous
+//    run of them (equal runs over all workgroups, so every CU has work), so a
+//    workgroup touches one or two experts (a few at small H), and its
+//    wavefronts take the run's items one at a time from a counter in LDS. (A
+//    SIMD issues for its oldest wavefront first: with fixed equal shares its
+//    four wavefronts finish one after another, ~47, 68, 93 and 105 us into a
+//    decode step, and the last quarter of the time runs with a quarter of the
+//    loads in flight. Taking items as they go, the wavefronts finish within
+//    about one item of each other.)
+//  - The down GEMM's B operand is h, one row per slot, so unlike gate/up the
+//    activations are not shared by every workgroup. Each workgroup stages the
+//    h rows of the slots of its experts into LDS (zero-padded to whole
+//    chunks) behind one barrier; if they do not fit, it runs phases of as many
+//    rows as fit, and an item's weights are streamed once per phase holding
+//    some of its slots.
+//  - Each wavefront then streams its items' weight chunks back to back, kP
+//    ahead in a register ring, across item boundaries; only weight loads and
+//    one scale-block load per item go through the vector-memory queue.
+//  - An item's scale bytes (16 * kNG rows x I/32 bytes) are contiguous and
+//    16-byte aligned: the wavefront loads them with a few 16-byte loads when
+//    its prefetch enters the item, copies them into its own LDS slot when it
+//    starts the item, and reads each chunk's pair from there. (A 2-byte load
+//    per chunk costs a whole memory instruction, and those instructions, not
+//    bytes, bound these kernels; the 90-byte scale rows of I = 2880 also rule
+//    out the 8-byte loads the gate/up kernel uses.)
+//  - The last chunk of a reduction axis that is not a multiple of 256 has
+//    lanes past the end: they read the row's first block with unit scale and
+//    meet the zero padding of the staged h rows, exactly as in the other
+//    kernel families.
+//  - Each output element sees the same MFMA sequence as in the other kernel
+//    families (same 256-element chunks, same lane-to-element map, same order
+//    from zero) and the same rounding, so a pick gives the same bits.
+#include "internal.h"
+#include "mxfp4_common.h"
+
+namespace moe {
+namespace {
+
+using namespace mx;
+
+constexpr int kWaves = 16;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kNG = 1;    // 16-row MFMA groups per item
+constexpr int kP = 5;     // weight chunks in flight per wavefront (ring of kP + 1)
+constexpr int kSbl = 2;   // 16-byte scale granules per lane per item (covers I <= 4096 / kNG)
+constexpr size_t kLdsMax = 160 * 1024;  // gfx950: the LDS of one CU
+
+struct Shape {
+  int nchunk, kpad, sbr, sbw;  // chunks, padded axis, scale bytes per row / per item
+};
+
+__host__ __device__ inline Shape shape_of(int I) {
+  Shape s;
+  s.nchunk = (I + kChunkElems - 1) / kChunkElems;
+  s.kpad = s.nchunk * kChunkElems;
+  s.sbr = I / 32;
+  s.sbw = kNG * 16 * s.sbr;
+  return s;
+}
+
+// LDS: h rows [max_rows][kpad] bf16 | per-wavefront scale slots [16][sbw] |
+// slot ids of the staged rows [max_rows].
+__host__ __device__ inline size_t lds_bytes(const Shape& s, int max_rows) {
+  return (size_t)max_rows * s.kpad * 2 + (size_t)kWaves * s.sbw + (size_t)max_rows * 4;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
+    const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
+    const int32_t* __restrict__ n_active, const int32_t* __restrict__ active_rows,
+    const int32_t* __restrict__ row_off, const int32_t* __restrict__ slots,
+    const __bf16* __restrict__ h, int H, int I, int max_rows, uint16_t* __restrict__ Y) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Shape sh = shape_of(I);
+  const int nchunk = sh.nchunk, kpad = sh.kpad, sbr = sh.sbr;
+  const int nblk = I / 32;
+  __bf16* hs = reinterpret_cast<__bf16*>(smem);
+  unsigned char* sc_all = smem + (size_t)max_rows * kpad * 2;
+  int* l_slot = reinterpret_cast<int*>(sc_all + (size_t)kWaves * sh.sbw);
+
+  const int tid = threadIdx.x;
+  const int na = __builtin_amdgcn_readfirstlane(*n_active);
+  const int per = H / (16 * kNG);  // items per expert
+  const int n = na * per;
+  if (n == 0) return;
+  const int qb = (n + gridDim.x - 1) / gridDim.x;  // items per workgroup
+  const int g0 = blockIdx.x * qb;
+  if (g0 >= n) return;  // the whole workgroup, before any barrier
+  const int g1 = min(n, g0 + qb);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __shared__ int l_next;  // next item of the workgroup's run not yet taken
+  const int s_lo = __builtin_amdgcn_readfirstlane(row_off[g0 / per]);
+  const int s_hi = __builtin_amdgcn_readfirstlane(row_off[(g1 - 1) / per + 1]);
+
+  const int lane = tid & 63, r = lane & 15, q = lane >> 4;
+  const size_t wrb = I / 2;
+  unsigned char* sc = sc_all + (size_t)wv * sh.sbw;  // this wavefront's scale slot
+  const int ngran = sh.sbw / 16;
+
+  for (int ph0 = s_lo; ph0 < s_hi; ph0 += max_rows) {
+    const int ph1 = min(s_hi, ph0 + max_rows);
+    if (ph0 != s_lo) __syncthreads();  // the previous phase is done with the rows
+    {
+      const int gpr = kpad / 8, nr = ph1 - ph0;
+      for (int gi = tid; gi < nr * gpr; gi += kThreads) {
+        const int m = gi / gpr, g = gi - m * gpr;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (g * 8 < I)
+          v = *reinterpret_cast<const uint4*>(h + (size_t)slots[ph0 + m] * I + g * 8);
+        *reinterpret_cast<uint4*>(hs + lds_elem(m, kpad, g * 8)) = v;
+      }
+      for (int i = tid; i < nr; i += kThreads) l_slot[i] = slots[ph0 + i];
+      if (tid == 0) l_next = g0;  // every phase walks the whole run again
+    }
+    __syncthreads();
+
+    // Slot positions of expert a inside this phase, and its 16-column passes.
+    auto lo_of = [&](int a) {
+      return max(__builtin_amdgcn_readfirstlane(row_off[a]), ph0);
+    };
+    auto ncols = [&](int a) {
+      return min(__builtin_amdgcn_readfirstlane(row_off[a + 1]), ph1) - lo_of(a);
+    };
+    auto passes_of = [&](int it) {
+      const int c = ncols(it / per);
+      return c > 0 ? (c + 15) >> 4 : 0;
+    };
+    // The next item of the run with slots in this phase, or g1 when none is
+    // left. One lane takes it from the counter; the value is wave-uniform.
+    auto take = [&]() {
+      int nx;
+      do {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(&l_next, 1);
+        nx = __builtin_amdgcn_readfirstlane(v);
+      } while (nx < g1 && passes_of(nx) == 0);
+      return nx < g1 ? nx : g1;
+    };
+    int p_it = take();
+    if (p_it >= g1) continue;  // the run is already taken
+
+    // Prefetch cursor: item, pass, chunk, this lane's weight row, and the
+    // item's scale block.
+    int p_pass = 0, p_c = 0, p_np = passes_of(p_it);
+    const uint8_t* pw;
+    const uint8_t* psb;
+    auto p_enter = [&](int it) {
+      const int a = it / per, o0 = (it - a * per) * 16 * kNG;
+      const size_t row = (uint32_t)__builtin_amdgcn_readfirstlane(active_rows[a]);
+      pw = w2 + (row * H + o0 + r) * wrb;
+      psb = s2 + (row * H + o0) * sbr;
+    };
+    p_enter(p_it);
+    // Move the cursor from the end of a pass to the start of the next pass or
+    // of the next item it takes. nchunk is a multiple of the ring length
+    // kP + 1, so this happens at one fixed ring position (first step of a
+    // pass's last cycle); everywhere else the cursor only steps to the next
+    // chunk. When no item is left the cursor restarts the current one (p_it
+    // unchanged tells the consumer to stop): the few loads still issued after
+    // that (fewer than nchunk) re-read cached chunks and are never used.
+    auto p_rollover = [&]() {
+      p_c = 0;
+      if (p_pass + 1 < p_np) {  // next 16 slots of the same item: its weights again
+        ++p_pass;
+        return;
+      }
+      const int nx = take();
+      if (nx < g1) {
+        p_pass = 0;
+        p_it = nx;
+        p_np = passes_of(nx);
+        p_enter(nx);
+      }
+    };
+    // Only the last chunk of the axis can have lanes past its end: they read
+    // the row's first block (its scale is replaced by unit).
+    const bool lane_in_last = (nchunk - 1) * kChunkBlocks + 2 * q < nblk;
+    const int off_last = lane_in_last ? (nchunk - 1) * 128 + 32 * q : 0;
+    // The scheduling barrier pins the loads at their place in the stream
+    // (left free, the compiler sinks them towards the end of a ring cycle,
+    // which shortens how far ahead they run).
+    auto load_w = [&](AChunk& a) {
+      const int off = p_c == nchunk - 1 ? off_last : p_c * 128 + 32 * q;
+      const uint4* p = reinterpret_cast<const uint4*>(pw + off);
+      a.lo = p[0];
+      a.hi = p[1];
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // The scale block of the cursor's item, kSbl granules per lane (separate
+    // variables: an array here ends up in scratch). Loaded at fixed points of
+    // the stream, never under a condition, so that the compiler can count the
+    // loads issued after it and waiting for it never waits for newer ones.
+    uint4 sblk0, sblk1;
+    // The scheduling barrier keeps the compiler from moving other loads
+    // ahead of it.
+    auto load_sblk = [&]() {
+      sblk0 = *reinterpret_cast<const uint4*>(psb + 16 * (lane < ngran ? lane : 0));
+      sblk1 = *reinterpret_cast<const uint4*>(psb + 16 * (lane + 64 < ngran ? lane + 64 : 0));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    AChunk ring[kP + 1];
+    load_sblk();
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+      load_w(ring[p]);
+      ++p_c;  // kP < nchunk
+    }
+
+    // The items the cursor took, and their passes, in order; nchunk is a
+    // multiple of kP + 1, so every pass starts at ring slot 0. In the last
+    // ring cycle of a pass the cursor, after its first advance, stands at the
+    // first chunk of the next pass or item: the scale block loaded there is
+    // the one the next pass uses (the same block again when the next pass is
+    // of the same item).
+    for (int it = p_it;;) {
+      const int np = passes_of(it);
+      const int a = it / per, o0 = (it - a * per) * 16 * kNG;
+      const int lo = lo_of(a), nt = ncols(a);
+      for (int pass = 0; pass < np; ++pass) {
+        if (pass == 0) {
+          // the item's scale block: registers -> this wavefront's LDS slot
+          // (lanes past the block hold granule 0, loaded from the clamped
+          // address, and write it back to granule 0: no branch, same bytes)
+          *reinterpret_cast<uint4*>(sc + 16 * (lane < ngran ? lane : 0)) = sblk0;
+          *reinterpret_cast<uint4*>(sc + 16 * (lane + 64 < ngran ? lane + 64 : 0)) = sblk1;
+          __builtin_amdgcn_wave_barrier();
+        }
+        const int j = pass * 16 + r;
+        const bool has = j < nt;
+        const int lrow = (has ? lo + j : lo) - ph0;  // staged h row of this column
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // One loop body for every ring cycle (a separate copy for the last
+        // cycle would keep the ring in other registers, and moving them
+        // between copies waits for every load in flight).
+        for (int c = 0; c < nchunk; c += kP + 1) {
+#pragma unroll
+          for (int u = 0; u <= kP; ++u) {
+            const int cc = c + u;
+            load_w(ring[(u + kP) % (kP + 1)]);
+            if (u == 0 && c + kP + 1 == nchunk) {
+              p_rollover();
+              load_sblk();
+            } else {
+              ++p_c;
+            }
+            const bool ok = cc != nchunk - 1 || lane_in_last;
+            const uint32_t raw =
+                *reinterpret_cast<const uint16_t*>(sc + (ok ? r * sbr + cc * 8 + 2 * q : 0));
+            const uint32_t b = ok ? raw : 0x7f7fu;
+            const float s0 = e8m0_to_f32(b & 0xffu), s1 = e8m0_to_f32(b >> 8);
+            const int e0 = cc * kChunkElems + 64 * q;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+              const bf16x8 bv =
+                  *reinterpret_cast<const bf16x8*>(hs + lds_elem(lrow, kpad, e0 + 8 * m));
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  dequant8(word_of(ring[u], m), m < 4 ? s0 : s1), bv, acc, 0, 0, 0);
+            }
+          }
+        }
+        // lane (r, q) holds output rows o0 + 4q + v of the pass's column r
+        if (has) {
+          const size_t sl = (uint32_t)l_slot[lrow];
+          uint32_t yb[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) yb[v] = f32_to_bf16_bits(acc[v]);
+          *reinterpret_cast<uint2*>(Y + sl * H + o0 + 4 * q) =
+              make_uint2(yb[0] | (yb[1] << 16), yb[2] | (yb[3] << 16));
+        }
+      }
+      if (p_it == it) break;  // the cursor found no further item
+      it = p_it;
+    }
+  }
+}
+
+// Rows of h one workgroup can stage, at most `want`.
+int rows_that_fit(const Shape& s, int want) {
+  const size_t dev = device_lds_per_block();
+  const size_t lim = dev < kLdsMax ? dev : kLdsMax;
+  const size_t fixed = (size_t)kWaves * s.sbw;
+  if (fixed >= lim) return 0;
+  const size_t per_row = (size_t)s.kpad * 2 + 4;
+  const size_t fit = (lim - fixed) / per_row;
+  return (int)(fit < (size_t)want ? fit : (size_t)want);
+}
+
+}  // namespace
+
+bool ffn_use_down_resident(int T, int k, int H, int I, const void* s2) {
+  const Shape s = shape_of(I);
+  return T >= 1 && I % 32 == 0 && H % (16 * kNG) == 0 && s.nchunk % (kP + 1) == 0 &&
+         s.sbw % 16 == 0 && s.sbw <= kSbl * 64 * 16 &&
+         (reinterpret_cast<uintptr_t>(s2) & 15u) == 0 && rows_that_fit(s, T * k) >= 1;
+}
+
+hipError_t launch_down_resident(const uint8_t* w2, const uint8_t* s2, int cap, int on_host,
+                                const moe_split& sp, int T, int k, int H, int I,
+                                const uint16_t* h_ws, uint16_t* Y, hipStream_t stream) {
+  (void)cap;
+  const Shape s = shape_of(I);
+  const int max_rows = rows_that_fit(s, T * k);
+  const int cus = device_cus();
+  const int grid = on_host ? kHostBankCUs : (cus > 2 * kHostBankCUs ? cus - kHostBankCUs : cus);
+  hipLaunchKernelGGL(ffn_down_resident, dim3(grid), dim3(kThreads), lds_bytes(s, max_rows),
+                     stream, w2, s2, sp.n_active, sp.active_rows, sp.row_off, sp.slots,
+                     reinterpret_cast<const __bf16*>(h_ws), H, I, max_rows, Y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -244,6 +244,28 @@ size_t lds_bytes(int K) {
 
 }  // namespace
 
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return cus;
+}
+
+size_t device_lds_per_block() {
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+      v <= 0) {
+    (void)hipGetLastError();
+    return 64 * 1024;
+  }
+  return (size_t)v;
+}
+
 int ffn_max_reduction() { return kLdsTile / (int)sizeof(uint16_t); }
 
 hipError_t launch_gate_up(const uint8_t* w13, const uint8_t* s13, int cap, int on_host,
@@ -268,6 +290,8 @@ hipError_t launch_down(const uint8_t* w2, const uint8_t* s2, int cap, int on_hos
                        uint16_t* Y, hipStream_t stream) {
   if (ffn_use_tiled(T, k, cap))
     return launch_down_tiled(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
+  if (ffn_use_down_resident(T, k, H, I, s2))
+    return launch_down_resident(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
   const int w = on_host ? kWavesHost : kWavesDevice;
   const int blocks = (H / (16 * kNG) + w - 1) / w;
   auto kern = on_host ? ffn_down<kPHost, kWavesHost> : ffn_down<kPDevice, kWavesDevice>;

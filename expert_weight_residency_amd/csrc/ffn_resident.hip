@@ -271,13 +271,7 @@ bool ffn_use_resident(int T, int k, int H, int cap, const void* s13) {
 hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int cap, int on_host,
                                    const moe_split& sp, const uint16_t* x, int T, int k, int H,
                                    int I, uint16_t* h_ws, hipStream_t stream) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0) {
-    (void)hipGetLastError();
-    cus = 256;
-  }
+  const int cus = device_cus();
   // A bank in host memory runs on kHostBankCUs workgroups (16 wavefronts,
   // 3 chunks each in flight: enough to fill the host link); a device bank on
   // the other CUs.

@@ -307,17 +307,6 @@ size_t tiled_lds_bytes(int cap) {
   return 2 * (size_t)kBufElems * sizeof(uint16_t) + ((size_t)cap + 1) * sizeof(int);
 }
 
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0) {
-    (void)hipGetLastError();
-    return 256;
-  }
-  return cus;
-}
-
 // Workgroups for a launch (items are grid-strided). A device bank gets one
 // workgroup per CU less the CUs a concurrent host-bank launch holds: a
 // workgroup that cannot be placed would run its share of the items after

@@ -63,6 +63,20 @@ hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int c
                                    const moe_split& split, const uint16_t* x, int T, int k, int H,
                                    int I, uint16_t* h_ws, hipStream_t stream);
 
+// Down GEMM as a persistent streaming kernel with the workgroup's h rows in
+// LDS (ffn_down_resident.hip): I a multiple of 32 whose chunk count is a
+// multiple of the ring length, a 16-byte aligned scale tensor; either bank.
+bool ffn_use_down_resident(int T, int k, int H, int I, const void* s2);
+hipError_t launch_down_resident(const uint8_t* w2, const uint8_t* s2, int cap, int on_host,
+                                const moe_split& split, int T, int k, int H, int I,
+                                const uint16_t* h_ws, uint16_t* Y, hipStream_t stream);
+
+// Compute units of the current device (256 if the query fails).
+int device_cus();
+// LDS bytes one workgroup may allocate on the current device (64 KB if the
+// query fails).
+size_t device_lds_per_block();
+
 // Average picks per launchable row from which the token-tiled kernels run.
 constexpr int kTiledMinPicksPerRow = 16;
 // Wavefronts that read a host-resident bank at once in the token-tiled kernels.
