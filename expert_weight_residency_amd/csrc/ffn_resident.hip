@@ -12,15 +12,16 @@
 //    the token of every slot) into LDS once, behind one barrier. After that
 //    no wavefront waits for another.
 //  - Work item = 16 i-columns of one active expert (its 16 gate rows and 16
-//    up rows). Each wavefront takes a contiguous run of items and streams
-//    their weight chunks back to back, kP chunks ahead in a register ring, so
-//    the prefetch runs straight across item boundaries. Inside the loop the
-//    only global loads are the weight chunks, issued unconditionally (past
-//    the wavefront's last chunk it re-reads its last 4 chunks, still in
-//    cache), so waiting for one chunk never waits for a newer one.
-//  - Exactly as many wavefronts run as make every run the same length
-//    (ceil(items / ceil(items / wavefronts))), so no wavefront has an extra
-//    item at the end; the idle ones are spread over the workgroups.
+//    up rows). Workgroup b owns one equal contiguous run of items, and its
+//    wavefronts take the run's items one at a time from a counter in LDS (a
+//    SIMD serves its oldest wavefront first, so fixed equal shares finish
+//    one after another and leave the last part of the launch with few loads
+//    in flight). Each wavefront streams its items' weight chunks back to
+//    back, kP chunks ahead in a register ring, so the prefetch runs straight
+//    across item boundaries. Inside the loop the only global loads are the
+//    weight chunks, issued unconditionally (past the wavefront's last chunk
+//    it re-reads its last 4 chunks, still in cache), so waiting for one chunk
+//    never waits for a newer one.
 //  - Scale bytes are loaded once per 4 chunks per row group (8 bytes per
 //    lane, one chunk's scales each) and redistributed across the lane
 //    quarters with two lane-swap instructions: a per-chunk 2-byte load per
@@ -90,6 +91,13 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
 
   const int tid = threadIdx.x;
   const int picks = T * k;
+  const int per = I / 16;  // items per expert
+  const int n = na * per;
+  const int qb = (n + gridDim.x - 1) / gridDim.x;  // items per workgroup
+  const int g0 = blockIdx.x * qb;
+  if (g0 >= n) return;  // the whole workgroup, before its barrier
+  const int g1 = min(n, g0 + qb);
+  __shared__ int l_next;  // next item of the workgroup's run not yet taken
   {
     const int gpr = kpad / 8;
     for (int gi = tid; gi < T * gpr; gi += kThreads) {
@@ -106,25 +114,24 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
       l_slot[i] = sl;
       l_tok[i] = sl / k;
     }
+    if (tid == 0) l_next = g0;
   }
   __syncthreads();
 
-  const int per = I / 16;  // items per expert
-  const int n = na * per;
-  if (n == 0) return;
-  const int W = gridDim.x * kWaves;
-  const int q_items = (n + W - 1) / W;
-  const int w_eff = (n + q_items - 1) / q_items;
   // Everything that steers the loop is wave-uniform; readfirstlane keeps it in
   // scalar registers (values read from LDS would otherwise count as per-lane
   // and turn the loop into exec-masked control flow).
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wid = wv * gridDim.x + blockIdx.x;
-  if (wid >= w_eff) return;  // no barrier follows
-  const int it0 = wid * q_items;
-  const int it1 = min(n, it0 + q_items);
-
   const int lane = tid & 63, r = lane & 15, q = lane >> 4;
+  // The next item of the workgroup's run (g1 once none is left); one lane
+  // takes it from the counter.
+  auto take = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&l_next, 1);
+    const int nx = __builtin_amdgcn_readfirstlane(v);
+    return nx < g1 ? nx : g1;
+  };
+  const int first = take();
+  if (first >= g1) return;  // the run is already taken; no barrier follows
   const int nchunk = H / kChunkElems;  // H is a multiple of 1024
   const size_t wrb = H / 2, srb = H / 32;
   const size_t rows_per_expert = 2 * (size_t)I;
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
   };
 
   // Prefetch cursor: item, pass, chunk, and this lane's two row pointers.
-  int p_it = it0, p_pass = 0, p_c = 0, p_npass = passes_of(it0);
+  int p_it = first, p_pass = 0, p_c = 0, p_npass = passes_of(first);
   const uint8_t* pw[kNG];
   const uint8_t* ps[kNG];
   auto p_rows = [&](int it) {
@@ -156,16 +163,20 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
     if (p_pass + 1 < p_npass) {  // next 16 tokens of the same item: its weights again
       p_c = 0;
       ++p_pass;
-    } else if (p_it + 1 < it1) {
-      p_c = 0;
-      p_pass = 0;
-      ++p_it;
-      p_rows(p_it);
-      p_npass = passes_of(p_it);
     } else {
-      // Past the wavefront's last chunk the loads only keep the stream
-      // unconditional: cycle through the last quad, which is still cached.
-      p_c = nchunk - 4;
+      const int nx = take();
+      if (nx < g1) {
+        p_c = 0;
+        p_pass = 0;
+        p_it = nx;
+        p_rows(nx);
+        p_npass = passes_of(nx);
+      } else {
+        // Past the wavefront's last chunk the loads only keep the stream
+        // unconditional: cycle through the last quad, which is still cached
+        // (p_it unchanged tells the consumer to stop).
+        p_c = nchunk - 4;
+      }
     }
   };
 
@@ -187,10 +198,11 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
     p_advance();
   }
 
-  // Items (and their 16-token passes) in order; nchunk is a multiple of 4,
-  // so every pass starts at ring slot 0 and quad boundary, and the prefetch
-  // cursor, P chunks ahead, crosses into the next pass without a pause.
-  for (int it = it0; it < it1; ++it) {
+  // The items the cursor took (and their 16-token passes) in order; nchunk is
+  // a multiple of 4, so every pass starts at ring slot 0 and quad boundary,
+  // and the prefetch cursor, P chunks ahead, crosses into the next pass or
+  // item without a pause.
+  for (int it = first;;) {
     const int a = it / per, i0 = (it - a * per) * 16;
     const int beg = __builtin_amdgcn_readfirstlane(l_off[a]);
     const int nt = __builtin_amdgcn_readfirstlane(l_off[a + 1]) - beg;
@@ -244,6 +256,8 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
             make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
       }
     }
+    if (p_it == it) break;  // the cursor took no further item
+    it = p_it;
   }
 }
 
