@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--no-policy", action="store_true", help="no counter reads or swaps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true")
+    ap.add_argument("--streams", choices=["cold-side", "hot-side"], default="hot-side",
+                    help="decode: which bank's FFN goes on the second stream (the other stays "
+                         "on the main stream with the split and the finalize)")
     ap.add_argument("--seed", type=int, default=20260917)
     ap.add_argument("--cold-path", default="staged", choices=["staged", "inplace"],
                     help="staged: copy the step's active cold rows into HBM with one contiguous "
@@ -146,7 +149,7 @@ def main():
 
     import expert_weight_residency_amd as moe
     import synth
-    from expert_weight_residency_amd.layer import ColdStage, LayerBuffers
+    from expert_weight_residency_amd.layer import ColdStage, LayerBuffers, enqueue_cold_ffn
     from expert_weight_residency_amd.policy import AdaptivePolicy
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -224,7 +227,11 @@ def main():
     bufs = LayerBuffers.allocate(T, k, H, I, n_hot, n_cold)
     stage = ColdStage(min(n_cold, T * k), H, I) if args.cold_path == "staged" else None
     main_s = torch.cuda.Stream()
-    cold_s = main_s if args.serial else torch.cuda.Stream()
+    side_s = main_s if args.serial else torch.cuda.Stream()
+    # --streams cold-side: the cold path on the side stream; hot-side: the hot
+    # FFN there and the cold path (the longer one in most decode steps) on the
+    # main stream with the split and the finalize
+    hot_s, cold_s = (side_s, main_s) if args.streams == "hot-side" else (main_s, side_s)
     policy = AdaptivePolicy(Lr, E)
     swaps = stale = 0
 
@@ -250,14 +257,8 @@ def main():
             e = torch.cuda.Event(enable_timing=True)
             e.record(cold_s)
             ev["c0"].append(e)
-        if stage is None:
-            moe.moe_expert_ffn_mxfp4(cold[l], bufs.cold_split, xc, k, I, bufs.workspace,
-                                     bufs.Y, stream=cold_s)
-        else:
-            staged = moe.moe_stage_rows(cold[l], bufs.cold_split, T, k, stage.bank, stage.rows,
-                                        H, I, stream=cold_s)
-            moe.moe_expert_ffn_mxfp4(stage.bank, staged, xc, k, I, bufs.workspace, bufs.Y,
-                                     stream=cold_s)
+        enqueue_cold_ffn(cold[l], bufs.cold_split, xc, k, H, I, bufs, stage, cold_s,
+                         overlap=not args.serial)
         if timed:
             e = torch.cuda.Event(enable_timing=True)
             e.record(cold_s)
@@ -268,6 +269,8 @@ def main():
             layer_call(s * lps + j, timed and j == 0)
 
     def layer_call(c, timed):
+        # hot_s runs the hot FFN, cold_s the cold path; the split and the
+        # finalize are on main_s, which is one of the two (or both, --serial)
         l = c % Lr
         xc = x_d[c % NX]
         moe.moe_route_split(ids_d[c], maps_dev[l], n_hot, n_cold, bufs.hot_split, bufs.cold_split,
@@ -276,25 +279,29 @@ def main():
             # cold bank first on its own stream: its 8 workgroups start beside the hot bank's
             cold_s.wait_stream(main_s)
             cold_ffn(c, l, timed)
+        if hot_s is not main_s:
+            hot_s.wait_stream(main_s)
         if timed:
             e = torch.cuda.Event(enable_timing=True)
-            e.record(main_s)
+            e.record(hot_s)
             ev["gu0"].append(e)
         moe.moe_expert_gate_up_mxfp4(hot[l], bufs.hot_split, xc, k, I, bufs.workspace,
-                                     stream=main_s)
+                                     stream=hot_s)
         if timed:
             e = torch.cuda.Event(enable_timing=True)
-            e.record(main_s)
+            e.record(hot_s)
             ev["gu1"].append(e)
         moe.moe_expert_down_mxfp4(hot[l], bufs.hot_split, T, k, H, I, bufs.workspace, bufs.Y,
-                                  stream=main_s)
+                                  stream=hot_s)
         if timed:
             e = torch.cuda.Event(enable_timing=True)
-            e.record(main_s)
+            e.record(hot_s)
             ev["dn1"].append(e)
         if cold_s is main_s:
             cold_ffn(c, l, timed)
-        else:
+        if hot_s is not main_s:
+            main_s.wait_stream(hot_s)
+        if cold_s is not main_s:
             main_s.wait_stream(cold_s)
         moe.moe_finalize(bufs.Y, w_d[c], bufs.out, stream=main_s)
 
@@ -391,6 +398,7 @@ def main():
                    "intermediate": I, "tokens": T, "hot_rows": n_hot, "cold_rows": n_cold,
                    "weights": "mxfp4", "cold_bank": COLD_BANK[args.cold_path], "map": args.map,
                    "layer_banks_rotated": Lr, "cold_stream": not args.serial,
+                   "streams": "serial" if args.serial else args.streams,
                    "policy": not args.no_policy},
         "us_per_layer": round(ms_per_step * 1e3 / lps, 1),
         "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
@@ -458,7 +466,7 @@ def run_prefill(args):
 
     import expert_weight_residency_amd as moe
     import synth
-    from expert_weight_residency_amd.layer import ColdStage, LayerBuffers
+    from expert_weight_residency_amd.layer import ColdStage, LayerBuffers, enqueue_cold_ffn
 
     E, k, H, I, T = 384, 6, 4096, 2880, 4096
     n_cold = 89
@@ -510,14 +518,8 @@ def run_prefill(args):
         if timed:
             rec("dn1", main_s)
             rec("c0", cold_s)
-        if stage is None:
-            moe.moe_expert_ffn_mxfp4(cold[l], bufs.cold_split, x_d[s], k, I, bufs.workspace,
-                                     bufs.Y, stream=cold_s)
-        else:
-            staged = moe.moe_stage_rows(cold[l], bufs.cold_split, T, k, stage.bank, stage.rows,
-                                        H, I, stream=cold_s)
-            moe.moe_expert_ffn_mxfp4(stage.bank, staged, x_d[s], k, I, bufs.workspace, bufs.Y,
-                                     stream=cold_s)
+        enqueue_cold_ffn(cold[l], bufs.cold_split, x_d[s], k, H, I, bufs, stage, cold_s,
+                         overlap=cold_s is not main_s)
         if timed:
             rec("c1", cold_s)
         if cold_s is not main_s:

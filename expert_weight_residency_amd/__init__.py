@@ -78,7 +78,7 @@ def lib():
                                             vp, vp, vp]
         L.moe_stage_rows.restype = i32
         L.moe_stage_rows.argtypes = [ctypes.POINTER(MoeBankC), MoeSplitC, i32, i32,
-                                     ctypes.POINTER(MoeBankC), vp, i32, i32, vp]
+                                     ctypes.POINTER(MoeBankC), vp, i32, i32, i32, vp]
         L.moe_finalize.restype = i32
         L.moe_finalize.argtypes = [vp, vp, i32, i32, i32, vp, vp]
         L.moe_usage_counts.restype = i32
@@ -205,13 +205,17 @@ def moe_expert_down_mxfp4(bank: Bank, split: Split, T: int, k: int, H: int, I: i
                                        workspace.data_ptr(), Y.data_ptr(), _stream(stream)))
 
 
+STAGE_GATE_UP, STAGE_DOWN, STAGE_ALL = 1, 2, 3
+
+
 def moe_stage_rows(src: Bank, split: Split, T: int, k: int, dst: Bank, dst_rows, H: int, I: int,
-                   stream=None) -> Split:
-    """Copy src's active rows (per split) to rows 0.. of the device bank dst;
+                   parts: int = STAGE_ALL, stream=None) -> Split:
+    """Copy src's active rows (per split) of the tensors `parts` names
+    (STAGE_GATE_UP, STAGE_DOWN, STAGE_ALL) to rows 0.. of the device bank dst;
     returns the split that drives the expert FFN on dst."""
     s, d = src.abi(), dst.abi()
     _check(lib().moe_stage_rows(ctypes.byref(s), split.abi(), T, k, ctypes.byref(d),
-                                dst_rows.data_ptr(), H, I, _stream(stream)))
+                                dst_rows.data_ptr(), H, I, int(parts), _stream(stream)))
     return Split(split.n_active, dst_rows, split.row_off, split.slots)
 
 

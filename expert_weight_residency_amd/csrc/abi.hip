@@ -178,8 +178,10 @@ int moe_expert_ffn_mxfp4(const moe_bank* bank, moe_split split, const uint16_t* 
 }
 
 int moe_stage_rows(const moe_bank* src, moe_split split, int T, int k, const moe_bank* dst,
-                   int32_t* dst_rows, int H, int I, void* stream) {
+                   int32_t* dst_rows, int H, int I, int parts, void* stream) {
   int rc;
+  if (parts < MOE_STAGE_GATE_UP || parts > MOE_STAGE_ALL)
+    return fail(MOE_EINVAL, "parts=%d must be 1 (gate/up), 2 (down) or 3 (both)", parts);
   if (T < 0) return fail(MOE_EINVAL, "T=%d must be >= 0", T);
   if (k < 1 || k > MOE_MAX_TOPK) return fail(MOE_EINVAL, "k=%d outside [1, %d]", k, MOE_MAX_TOPK);
   if ((int64_t)T * k >= (int64_t)1 << 31) return fail(MOE_EINVAL, "T*k too large");
@@ -198,10 +200,12 @@ int moe_stage_rows(const moe_bank* src, moe_split split, int T, int k, const moe
   const uint8_t* sp[4];
   const uint8_t* dq[4];
   if ((rc = bank_device_ptrs(src, sp)) || (rc = bank_device_ptrs(dst, dq))) return rc;
-  const uint64_t rb[4] = {(uint64_t)2 * I * (H / 2), (uint64_t)2 * I * (H / 32),
-                          (uint64_t)H * (I / 2), (uint64_t)H * (I / 32)};
+  // row bytes of each tensor; zero for a tensor this call does not copy
+  const bool gu = parts & MOE_STAGE_GATE_UP, dn = parts & MOE_STAGE_DOWN;
+  const uint64_t rb[4] = {gu ? (uint64_t)2 * I * (H / 2) : 0, gu ? (uint64_t)2 * I * (H / 32) : 0,
+                          dn ? (uint64_t)H * (I / 2) : 0, dn ? (uint64_t)H * (I / 32) : 0};
   for (int t = 0; t < 4; ++t)
-    if ((reinterpret_cast<uintptr_t>(sp[t]) | reinterpret_cast<uintptr_t>(dq[t])) & 15u)
+    if (rb[t] && ((reinterpret_cast<uintptr_t>(sp[t]) | reinterpret_cast<uintptr_t>(dq[t])) & 15u))
       return fail(MOE_EINVAL, "bank tensor %d must be 16-byte aligned for staging", t);
   uint8_t* dp[4] = {const_cast<uint8_t*>(dq[0]), const_cast<uint8_t*>(dq[1]),
                     const_cast<uint8_t*>(dq[2]), const_cast<uint8_t*>(dq[3])};

@@ -22,7 +22,7 @@ constexpr uint64_t kPiece = kThreads * kUnroll;     // granules per piece (64 KB
 
 // The copy is cut into pieces of 64 KB (the last piece of a tensor row may be
 // shorter): per active row, ceil(row bytes / 64 KB) pieces of each tensor in
-// turn. Workgroup b takes pieces b, b + G, ...; in a piece each thread moves
+// turn (none for a tensor passed with zero row bytes: not copied). Workgroup b takes pieces b, b + G, ...; in a piece each thread moves
 // 4 granules, consecutive lanes on consecutive granules. (Measured on the
 // host link: 8 x 1024 threads with 4 granules in flight per thread stream at
 // the link's rate; 8 in flight or 256-thread workgroups fall short.)

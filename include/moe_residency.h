@@ -167,12 +167,17 @@ int moe_expert_gate_up_mxfp4(const moe_bank *bank, moe_split split, const uint16
 int moe_expert_down_mxfp4(const moe_bank *bank, moe_split split, int T, int k, int H, int I,
                           const void *workspace, uint16_t *Y, void *stream);
 
+/* moe_stage_rows parts: the gate/up tensors (w13, s13), the down tensors (w2, s2). */
+#define MOE_STAGE_GATE_UP 1
+#define MOE_STAGE_DOWN 2
+#define MOE_STAGE_ALL 3
+
 /*
  * moe_stage_rows -- copy one bank's active rows into a compact device bank.
  *
  * For a = 0 .. n_active-1 (n_active = *split.n_active on the device): row
- * split.active_rows[a] of each of the four tensors of `src` is copied to row a
- * of `dst`, and dst_rows[a] = a. The split {split.n_active, dst_rows,
+ * split.active_rows[a] of each tensor of `src` that `parts` names is copied to
+ * row a of the same tensor of `dst`, and dst_rows[a] = a. The split {split.n_active, dst_rows,
  * split.row_off, split.slots} then drives moe_expert_ffn_mxfp4 on `dst` with
  * results identical to `split` on `src` (the FFN arithmetic does not depend on
  * the bank). For a cold bank in pinned host memory this replaces the FFN's
@@ -184,12 +189,15 @@ int moe_expert_down_mxfp4(const moe_bank *bank, moe_split split, int T, int k, i
  * src: the bank the split was made for (host or device). split: its
  * moe_route_split output for a step of T tokens, k picks each. dst: a device
  * bank (on_host = 0) with n_rows >= min(src->n_rows, T*k); rows past n_active
- * are left unwritten. dst_rows: device int32 [min(src->n_rows, T*k)]. All
- * tensors 16-byte aligned. Launches one kernel; nothing when T == 0 or src has
- * no rows.
+ * are left unwritten. dst_rows: device int32 [min(src->n_rows, T*k)]. parts:
+ * MOE_STAGE_GATE_UP, MOE_STAGE_DOWN or both (MOE_STAGE_ALL); the tensors it
+ * names 16-byte aligned. Staging the two parts in two calls lets the gate/up
+ * GEMM on dst start while the down tensors are still being copied. Launches
+ * one kernel; nothing when T == 0 or src has no rows. MOE_EINVAL for a parts
+ * value outside 1..3, before any work is enqueued.
  */
 int moe_stage_rows(const moe_bank *src, moe_split split, int T, int k, const moe_bank *dst,
-                   int32_t *dst_rows, int H, int I, void *stream);
+                   int32_t *dst_rows, int H, int I, int parts, void *stream);
 
 /*
  * moe_finalize -- ordered fp32 FMA combine of the k rows of each token.

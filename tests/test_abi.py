@@ -71,6 +71,40 @@ def test_ffn_rejects_bad_shapes(L):
     assert L.moe_expert_ffn_mxfp4(ctypes.byref(bank), _split(), p, 0, 2, 256, 128, p, p, None) == moe.MOE_OK
 
 
+def test_stage_rows_rejects_bad_args(L):
+    """Argument errors of moe_stage_rows come back before any GPU call (device
+    banks: no pointer translation either)."""
+    p = 0x1000
+    src = moe.MoeBankC(p, p, p, p, 10, 0)
+    dst = moe.MoeBankC(p, p, p, p, 10, 0)
+    rows = p
+
+    def call(src_=src, dst_=dst, T=4, k=2, H=256, I=128, parts=moe.STAGE_ALL, split=None):
+        return L.moe_stage_rows(ctypes.byref(src_) if src_ is not None else None,
+                                split or _split(), T, k,
+                                ctypes.byref(dst_) if dst_ is not None else None, rows, H, I,
+                                parts, None)
+
+    for parts in (0, 4, -1):
+        assert call(parts=parts) == moe.MOE_EINVAL
+        assert "parts" in moe.moe_last_error()
+    assert call(k=0) == moe.MOE_EINVAL
+    assert call(H=100) == moe.MOE_EINVAL
+    assert call(src_=None) == moe.MOE_EINVAL
+    assert call(dst_=None) == moe.MOE_EINVAL
+    assert call(dst_=moe.MoeBankC(p, p, p, p, 10, 1)) == moe.MOE_EINVAL  # dst in host memory
+    assert "device bank" in moe.moe_last_error()
+    # the split can name min(10, 4*2) = 8 rows; a 7-row stage is too small
+    assert call(dst_=moe.MoeBankC(p, p, p, p, 7, 0)) == moe.MOE_EINVAL
+    assert call(split=_split(0)) == moe.MOE_EINVAL
+    # a scale tensor off 16-byte alignment is refused only when its part is staged
+    odd = moe.MoeBankC(p, p + 2, p, p, 10, 0)
+    assert call(src_=odd, parts=moe.STAGE_GATE_UP) == moe.MOE_EINVAL
+    assert "aligned" in moe.moe_last_error()
+    assert call(src_=odd, T=0) == moe.MOE_OK  # nothing to do: no launch, no error
+    assert call(src_=moe.MoeBankC(p, p, p, p, 0, 0)) == moe.MOE_OK
+
+
 def test_finalize_and_counts_reject_bad_args(L):
     p = 0x1000
     assert L.moe_finalize(p, p, 4, 2, 12, p, None) == moe.MOE_EINVAL

@@ -2,9 +2,11 @@
 compact HBM bank before the cold FFN.
 
 Bit-exact: the staged rows equal the source rows the split names, the staged
-row list is 0..n_active-1, and a layer run through the stage gives the same Y
-rows and output as the in-place run (small shape, and the full shape with the
-fitted map and 16 decode tokens), including a step with no cold picks.
+row list is 0..n_active-1, staging one part (gate/up or down tensors) leaves
+the other untouched, and a layer run through the stage gives the same Y rows
+and output as the in-place run (small shape on one stream and with either
+bank's FFN on a side stream, and the full shape with the fitted map and 16
+decode tokens), including a step with no cold picks.
 """
 import numpy as np
 import pytest
@@ -29,12 +31,12 @@ def log(msg):
     print(msg, flush=True)
 
 
-def _run(hot, cold, rm, ids, w, x, H, I, stage, cold_stream=None):
+def _run(hot, cold, rm, ids, w, x, H, I, stage, cold_stream=None, hot_stream=None):
     T, k = ids.shape
     ids_d, w_d, x_d = routing_tensors(ids, w, x)
     bufs = LayerBuffers.allocate(T, k, H, I, hot.n_rows, cold.n_rows)
     layer = ResidencyLayer(hot, cold, torch.from_numpy(rm).cuda(), H, I, stage=stage)
-    layer.forward(x_d, ids_d, w_d, bufs, cold_stream=cold_stream)
+    layer.forward(x_d, ids_d, w_d, bufs, cold_stream=cold_stream, hot_stream=hot_stream)
     torch.cuda.synchronize()
     return (bufs.Y[: T * k].cpu().numpy().copy(), bufs.out[:T].cpu().numpy().copy(), bufs)
 
@@ -63,18 +65,53 @@ def test_stage_copies_named_rows():
         assert np.array_equal(got, cold_arr[name][active]), name
 
 
-@pytest.mark.parametrize("two_streams", [False, True])
-def test_staged_layer_equals_in_place_bitwise(two_streams):
+@pytest.mark.parametrize("streams", ["one", "cold_side", "hot_side"])
+def test_staged_layer_equals_in_place_bitwise(streams):
+    """The staged cold path (on two streams: gate/up tensors staged first, the
+    gate/up GEMM on them beside the copy of the down tensors) gives the bits of
+    the in-place path, whichever bank's FFN runs on the side stream."""
     E, k, H, I, T = 32, 4, 1024, 512, 24
     rm, ho, co = synth.random_map(E, 10, 5)
     hot = device_bank(host_bank(ho, 5, 0, H, I))
     cold = pinned_bank(host_bank(co, 5, 0, H, I))
     ids, w = synth.skewed_routing(T, k, E, 5, 0, 0)
     x = synth.activations(T, H, 5)
-    cs = torch.cuda.Stream() if two_streams else None
-    Y0, o0, _ = _run(hot, cold, rm, ids, w, x, H, I, None, cs)
-    Y1, o1, _ = _run(hot, cold, rm, ids, w, x, H, I, ColdStage(min(10, T * k), H, I), cs)
+    side = {"cold_stream": torch.cuda.Stream()} if streams == "cold_side" else (
+        {"hot_stream": torch.cuda.Stream()} if streams == "hot_side" else {})
+    log(f"staged layer, streams={streams}")
+    Y0, o0, _ = _run(hot, cold, rm, ids, w, x, H, I, None)
+    Y1, o1, _ = _run(hot, cold, rm, ids, w, x, H, I, ColdStage(min(10, T * k), H, I), **side)
     assert np.array_equal(Y0, Y1) and np.array_equal(o0, o1)
+
+
+def test_stage_parts():
+    """Staging the gate/up tensors leaves the down tensors of the stage
+    untouched; staging the down tensors then completes the rows."""
+    E, k, H, I, T = 24, 3, 512, 320, 12
+    rm, ho, co = synth.random_map(E, 9, 31)
+    cold_arr = host_bank(co, 31, 0, H, I)
+    cold = pinned_bank(cold_arr)
+    ids, _ = synth.skewed_routing(T, k, E, 31, 0, 0)
+    hs, cs = moe.Split.empty(E - 9, T, k), moe.Split.empty(9, T, k)
+    ninv = torch.zeros(1, dtype=torch.int32, device="cuda")
+    moe.moe_route_split(torch.from_numpy(ids).cuda(), torch.from_numpy(rm).cuda(), E - 9, 9, hs, cs,
+                        ninv)
+    stage = ColdStage(min(9, T * k), H, I)
+    for t in stage.bank.tensors().values():
+        t.fill_(0xA5)
+    moe.moe_stage_rows(cold, cs, T, k, stage.bank, stage.rows, H, I, parts=moe.STAGE_GATE_UP)
+    torch.cuda.synchronize()
+    active, _, _ = cs.to_host()
+    n = len(active)
+    assert n > 0
+    for name in ("w13", "s13"):
+        assert np.array_equal(getattr(stage.bank, name)[:n].cpu().numpy(), cold_arr[name][active])
+    for name in ("w2", "s2"):
+        assert (getattr(stage.bank, name).cpu().numpy() == 0xA5).all(), name
+    moe.moe_stage_rows(cold, cs, T, k, stage.bank, stage.rows, H, I, parts=moe.STAGE_DOWN)
+    torch.cuda.synchronize()
+    for name in ("w13", "s13", "w2", "s2"):
+        assert np.array_equal(getattr(stage.bank, name)[:n].cpu().numpy(), cold_arr[name][active])
 
 
 def test_staged_full_shape_decode_bitwise():
@@ -95,6 +132,7 @@ def test_staged_full_shape_decode_bitwise():
         x = synth.activations(T, H, 7, 0, step)
         n_cold_picks = int((rm[ids] < 0).sum())
         log(f"full shape step {step}: {n_cold_picks} cold picks")
-        Y0, o0, _ = _run(hb, cb, rm, ids, w, x, H, I, None, torch.cuda.Stream())
-        Y1, o1, _ = _run(hb, cb, rm, ids, w, x, H, I, stage, torch.cuda.Stream())
+        side = "hot_stream" if step == 1 else "cold_stream"
+        Y0, o0, _ = _run(hb, cb, rm, ids, w, x, H, I, None, **{side: torch.cuda.Stream()})
+        Y1, o1, _ = _run(hb, cb, rm, ids, w, x, H, I, stage, **{side: torch.cuda.Stream()})
         assert np.array_equal(Y0, Y1) and np.array_equal(o0, o1)
