@@ -33,9 +33,10 @@
 //    bytes, bound these kernels; the 90-byte scale rows of I = 2880 also rule
 //    out the 8-byte loads the gate/up kernel uses.)
 //  - The last chunk of a reduction axis that is not a multiple of 256 has
-//    lanes past the end: they read the row's first block with unit scale and
-//    meet the zero padding of the staged h rows, exactly as in the other
-//    kernel families.
+//    lanes past the end: they read that chunk's first block with unit scale
+//    and meet the zero padding of the staged h rows (the other kernel
+//    families read the row's first block instead; finite values times zero,
+//    accumulated from +0, give the same bits either way).
 //  - Each output element sees the same MFMA sequence as in the other kernel
 //    families (same 256-element chunks, same lane-to-element map, same order
 //    from zero) and the same rounding, so a pick gives the same bits.
@@ -181,9 +182,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
       }
     };
     // Only the last chunk of the axis can have lanes past its end: they read
-    // the row's first block (its scale is replaced by unit).
+    // the chunk's first block (in the same cache line as the lanes in range,
+    // where the row's first block would cost a second fetch of a line read
+    // long before); their scale is replaced by unit and their activations are
+    // the zero padding, so what they read does not change a bit of the result
+    // (finite E2M1 values times zero, accumulated from +0).
     const bool lane_in_last = (nchunk - 1) * kChunkBlocks + 2 * q < nblk;
-    const int off_last = lane_in_last ? (nchunk - 1) * 128 + 32 * q : 0;
+    const int off_last = (nchunk - 1) * 128 + (lane_in_last ? 32 * q : 0);
     // The scheduling barrier pins the loads at their place in the stream
     // (left free, the compiler sinks them towards the end of a ring cycle,
     // which shortens how far ahead they run).
