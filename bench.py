@@ -120,6 +120,11 @@ def measure_ceilings(torch):
     t = timed(lambda: L.ceiling_stream_read(dev.data_ptr(), dev.numel(), sink.data_ptr(), blocks,
                                             ctypes.c_void_p(s.cuda_stream)), 5)
     out["hbm_read_GBps"] = round(dev.numel() / t / 1e9, 1)
+    L.ceiling_stream_read_nt.argtypes = L.ceiling_stream_read.argtypes
+    L.ceiling_stream_read_nt.restype = ctypes.c_int
+    t = timed(lambda: L.ceiling_stream_read_nt(dev.data_ptr(), dev.numel(), sink.data_ptr(),
+                                               blocks, ctypes.c_void_p(s.cuda_stream)), 5)
+    out["hbm_read_nontemporal_GBps"] = round(dev.numel() / t / 1e9, 1)
     del dev
     host = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
     hp = device_pointer(host)
