@@ -67,13 +67,20 @@ def parse():
                          "stream each (moe_stage_rows), then run the cold FFN from HBM; inplace: "
                          "the cold FFN reads the pinned host bank directly")
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "step40", "highconc", "offdomain"],
+                    choices=["decode", "prefill", "step40", "highconc", "offdomain",
+                             "domainshift"],
                     help="decode: the default line (one layer of 16 tokens per step); prefill: "
                          "one 4096-token chunk per step (counter off), with the hot bank's MFMA "
                          "utilisation; step40: 40 layer calls of 7 tokens per step; highconc: "
                          "112 tokens per step (--map fitted or positional); offdomain: 7 tokens, "
                          "map fitted to one ranking, traffic from another, the adaptive policy "
-                         "moving experts, reported in windows")
+                         "moving experts, reported in windows; domainshift: 7 tokens, traffic "
+                         "from the map's ranking, then another, then the first again (equal "
+                         "phases), the policy following, then a restore to the boot map")
+    ap.add_argument("--ctrl", default=None,
+                    help="runtime control file (JSON) read at every policy barrier: freeze, "
+                         "counting, budgets, dump_counts, restore_map")
+    ap.add_argument("--telemetry", default=None, help="append one JSON line per policy barrier")
     return ap.parse_args()
 
 
@@ -155,13 +162,14 @@ def main():
     import expert_weight_residency_amd as moe
     import synth
     from expert_weight_residency_amd.layer import ColdStage, LayerBuffers, enqueue_cold_ffn
-    from expert_weight_residency_amd.policy import AdaptivePolicy
+    from expert_weight_residency_amd.policy import (AdaptivePolicy, RuntimeControl, Telemetry,
+                                                    restore_swaps)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.lib()
     if args.workload == "prefill":
         return run_prefill(args)
-    lps, off_domain, wname = 1, False, None
+    lps, off_domain, shift, wname = 1, False, False, None
     if args.workload == "step40":
         args.tokens, lps = 7, 40
         args.steps, args.warmup = min(args.steps, 32), min(args.warmup, 4)
@@ -176,6 +184,11 @@ def main():
         args.tokens, off_domain, lps = 7, True, args.layers
         args.steps, args.warmup = 1536, min(args.warmup, 8)
         wname = f"off_domain_decode_t7_{args.layers}_layers"
+    elif args.workload == "domainshift":
+        # three equal phases: the map's own ranking (A), a second ranking (B), A again
+        args.tokens, shift, lps = 7, True, args.layers
+        args.steps, args.warmup = 1536, min(args.warmup, 8)
+        wname = f"domain_shift_a_b_a_decode_t7_{args.layers}_layers"
     E, k, H, I, T = 384, 6, 4096, 2880, args.tokens
     n_cold = 89
     n_hot = E - n_cold
@@ -218,12 +231,20 @@ def main():
     C = S * lps
     perms = [synth.layer_permutation(E, seed ^ 0x0FFD0 if off_domain else seed, l)
              for l in range(Lr)]
+    perms_b = [synth.layer_permutation(E, seed ^ 0x0FFD0, l) for l in range(Lr)]
+    phase_len = args.steps // 3
+
+    def phase_of(c):  # domain-shift phase of layer call c: 0 (A), 1 (B), 2 (A)
+        i = c // lps - args.warmup
+        return 0 if i < phase_len else (1 if i < 2 * phase_len else 2)
+
     ids_np = np.empty((C, T, k), np.int32)
     w_np = np.empty((C, T, k), np.float32)
     NX = min(C, 64)
     x_np = np.empty((NX, T, H), np.uint16)
     for c in range(C):
-        ids_np[c], w_np[c] = synth.skewed_routing(T, k, E, seed, c % Lr, c, perm=perms[c % Lr])
+        pm = perms_b[c % Lr] if shift and phase_of(c) == 1 else perms[c % Lr]
+        ids_np[c], w_np[c] = synth.skewed_routing(T, k, E, seed, c % Lr, c, perm=pm)
     for c in range(NX):
         x_np[c] = synth.activations(T, H, seed, c % Lr, c)
     ids_d = torch.from_numpy(ids_np).cuda()
@@ -238,9 +259,12 @@ def main():
     # main stream with the split and the finalize
     hot_s, cold_s = (side_s, main_s) if args.streams == "hot-side" else (main_s, side_s)
     policy = AdaptivePolicy(Lr, E)
+    control = RuntimeControl(policy, args.ctrl)
+    telemetry = Telemetry(args.telemetry)
+    boot_hot = [h.copy() for h in hot_owner]
     swaps = stale = 0
 
-    ev = {name: [] for name in ("gu0", "gu1", "dn1", "c0", "c1")}
+    ev = {name: [] for name in ("gu0", "gu1", "dn1", "c0", "c1", "s0", "s1")}
     bytes_step, hot_bytes_gu, cold_bytes, uh_list, uc_list, cold_picks = [], [], [], [], [], 0
 
     def account(c, rm):
@@ -270,8 +294,16 @@ def main():
             ev["c1"].append(e)
 
     def step(s, timed):
+        if timed:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(main_s)
+            ev["s0"].append(e)
         for j in range(lps):
             layer_call(s * lps + j, timed and j == 0)
+        if timed:
+            e = torch.cuda.Event(enable_timing=True)
+            e.record(main_s)
+            ev["s1"].append(e)
 
     def layer_call(c, timed):
         # hot_s runs the hot FFN, cold_s the cold path; the split and the
@@ -279,7 +311,8 @@ def main():
         l = c % Lr
         xc = x_d[c % NX]
         moe.moe_route_split(ids_d[c], maps_dev[l], n_hot, n_cold, bufs.hot_split, bufs.cold_split,
-                            bufs.n_invalid, counts[l], 256, stream=main_s)
+                            bufs.n_invalid, counts[l] if control.counting else None, 256,
+                            stream=main_s)
         if cold_s is not main_s:
             # cold bank first on its own stream: its 8 workgroups start beside the hot bank's
             cold_s.wait_stream(main_s)
@@ -310,23 +343,44 @@ def main():
             main_s.wait_stream(cold_s)
         moe.moe_finalize(bufs.Y, w_d[c], bufs.out, stream=main_s)
 
-    def barrier():
+    def apply_swaps(props):
+        """Apply proposals between steps; returns (applied, refused as stale)."""
         nonlocal swaps, stale
-        moe.moe_usage_counts(counts, snap, stream=main_s)
-        main_s.synchronize()
-        policy.observe(snap.numpy())
-        for sw in policy.decide(hot_owner, cold_owner):
+        ok = bad = 0
+        for sw in props:
             l = sw.layer
             try:
                 moe.moe_swap_rows(hot[l], cold[l], sw.hot_row, sw.cold_row, sw.expect_hot_expert,
                                   sw.expect_cold_expert, maps_dev[l], hot_owner[l], cold_owner[l],
                                   staging, H, I, stream=main_s)
             except moe.MoeStale:
-                stale += 1
+                bad += 1
                 continue
             maps_host[l][sw.expect_hot_expert] = -1 - sw.cold_row
             maps_host[l][sw.expect_cold_expert] = sw.hot_row
-            swaps += 1
+            ok += 1
+        swaps += ok
+        stale += bad
+        return ok, bad
+
+    def barrier(step):
+        unknown = control.poll()
+        moe.moe_usage_counts(counts, snap, stream=main_s)
+        main_s.synchronize()
+        control.maybe_dump(snap.numpy())
+        policy.observe(snap.numpy())
+        if control.restore_pending:
+            props = restore_swaps(hot_owner, cold_owner, boot_hot,
+                                  limit=policy.cfg.swaps_per_barrier)
+            if not props:
+                control.restore_pending = False
+        else:
+            props = policy.decide(hot_owner, cold_owner)
+        ok, bad = apply_swaps(props)
+        telemetry.log(step=step, proposed=len(props), applied=ok, stale=bad,
+                      frozen=policy.frozen, counting=control.counting,
+                      restoring=control.restore_pending,
+                      **({"unknown_ctrl_keys": unknown} if unknown else {}))
 
     with torch.cuda.stream(main_s):
         for s in range(args.warmup):
@@ -353,12 +407,13 @@ def main():
             step(s, True)
             if not args.no_policy and (s + 1) % policy.cfg.read_every == 0:
                 before = swaps
-                barrier()
+                barrier(s + 1)
                 win_swaps += swaps - before
-            if off_domain and (i + 1) % 128 == 0:
+            if (off_domain or shift) and (i + 1) % 128 == 0:
                 torch.cuda.synchronize()
                 now = time.perf_counter()
                 windows.append({"steps": [i - 127, i + 1],
+                                **({"phase": "ABA"[phase_of(s * lps)]} if shift else {}),
                                 "cold_share_of_picks": round(win_cold / win_picks, 4),
                                 "us_per_layer": round((now - win_t) * 1e6 / (128 * lps), 1),
                                 "swaps_applied": win_swaps})
@@ -371,6 +426,28 @@ def main():
     gu_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["gu0"], ev["gu1"])])
     dn_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["gu1"], ev["dn1"])])
     c_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["c0"], ev["c1"])])
+    st_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["s0"], ev["s1"])])
+
+    def pct(v):  # p10 / median / p90 in microseconds
+        return ({k: round(float(np.percentile(v, q) * 1e3), 1)
+                 for k, q in (("p10", 10), ("p50", 50), ("p90", 90))} if len(v) else None)
+
+    # domain shift: after the timed phases, queue a restore to the boot-time map
+    # and apply it between (untimed) barriers, as the control file's restore_map does
+    restore = None
+    if shift and not args.no_policy:
+        before, rounds = swaps, 0
+        control.restore_pending = True
+        with torch.cuda.stream(main_s):
+            while control.restore_pending and rounds < 1000:
+                barrier(-1)
+                rounds += 1
+        torch.cuda.synchronize()
+        restore = {"swaps": swaps - before, "barriers": rounds,
+                   "hot_sets_equal_boot": all(set(h.tolist()) == set(b.tolist())
+                                              for h, b in zip(hot_owner, boot_hot)),
+                   "device_maps_equal_host": all(
+                       np.array_equal(maps_dev[l].cpu().numpy(), maps_host[l]) for l in range(Lr))}
     achieved = float(np.sum(hot_bytes_gu) / (gu_ms.sum() / 1e3) / 1e9)
     value = float(np.mean(bytes_step) / (ms_per_step / 1e3) / 1e9)
     cold_link = float(np.sum(cold_bytes) / max(c_ms.sum() / 1e3, 1e-12) / 1e9)
@@ -398,8 +475,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wname or f"full_layer_decode_t{T}", "experts": E, "top_k": k,
-                   "hidden": H, "layers_per_step": lps, "traffic": "off-domain" if off_domain
-                   else "in-domain",
+                   "hidden": H, "layers_per_step": lps,
+                   "traffic": ("off-domain" if off_domain else
+                               "domain shift A-B-A" if shift else "in-domain"),
                    "intermediate": I, "tokens": T, "hot_rows": n_hot, "cold_rows": n_cold,
                    "weights": "mxfp4", "cold_bank": COLD_BANK[args.cold_path], "map": args.map,
                    "layer_banks_rotated": Lr, "cold_stream": not args.serial,
@@ -418,7 +496,10 @@ def main():
                     "cold_unique_per_step": round(float(np.mean(uc_list)), 2),
                     "cold_share_of_picks": round(cold_picks / (K * lps * T * k), 4)},
         "swaps_applied": swaps, "swaps_stale": stale,
-        **({"windows": windows} if off_domain else {}),
+        **({"windows": windows} if (off_domain or shift) else {}),
+        **({"restore": restore} if restore else {}),
+        "percentiles_us": {name: pct(v) for name, v in (("step", st_ms), ("hot_gate_up", gu_ms),
+                                                        ("hot_down", dn_ms), ("cold_path", c_ms))},
         "ceilings": ceilings,
         "roofline": {"kernel": "ffn_gate_up_resident (hot bank)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",

@@ -12,12 +12,24 @@ the busiest cold experts in exchange for the idlest hot ones, at most
 rows and the experts it was decided against, so moe_swap_rows can refuse it if
 the owners changed in between.
 
+Runtime control (same section: a small JSON file that freezes adaptation,
+turns counting on or off, changes budgets, dumps counts or queues a restore to
+the boot-time map): RuntimeControl reads such a file when it changes and
+applies it to the policy; restore_swaps() lists the swaps that bring every
+layer back to its boot-time hot set; Telemetry appends JSON lines per barrier
+and per swap.
+
 Readings of the pages: the average is kept in counts per read window; "minimum
-average 8" applies to the promoted expert's average.
+average 8" applies to the promoted expert's average; a restore brings back the
+boot-time hot/cold membership of every expert (a hot-cold swap moves one
+expert each way, so the rows an expert ends up in may differ from its boot
+rows; the row map always says where its weights are).
 """
 from __future__ import annotations
 
-from dataclasses import dataclass
+import json
+import os
+from dataclasses import dataclass, fields
 
 import numpy as np
 
@@ -47,6 +59,7 @@ class AdaptivePolicy:
         self.cfg = cfg or PolicyConfig()
         self.avg = np.zeros((layers, experts), np.float64)
         self.prev = None
+        self.frozen = False  # observe() keeps averaging; decide() proposes nothing
         self.decay = 0.5 ** (self.cfg.read_every / self.cfg.half_life)
 
     def observe(self, snapshot: np.ndarray) -> None:
@@ -62,6 +75,8 @@ class AdaptivePolicy:
     def decide(self, hot_owner: list, cold_owner: list) -> list:
         """hot_owner[l] / cold_owner[l]: int arrays, expert held by each row."""
         c = self.cfg
+        if self.frozen:
+            return []
         props = []
         for layer, (ho, co) in enumerate(zip(hot_owner, cold_owner)):
             if len(ho) == 0 or len(co) == 0:
@@ -76,3 +91,93 @@ class AdaptivePolicy:
                     props.append(Swap(layer, r, b, eh, ec, float(a[ec] - a[eh])))
         props.sort(key=lambda s: -s.gain)
         return props[: c.swaps_per_barrier]
+
+
+def restore_swaps(hot_owner: list, cold_owner: list, boot_hot_owner: list,
+                  limit: int | None = None) -> list:
+    """Swaps that return every layer to its boot-time hot set: each expert that
+    is hot now but was cold at boot is exchanged with one that is cold now but
+    was hot at boot (both in ascending expert order). At most `limit` swaps in
+    total (None: all); call again after applying them until none are left."""
+    props = []
+    for layer, (ho, co, bh) in enumerate(zip(hot_owner, cold_owner, boot_hot_owner)):
+        boot_hot = set(int(e) for e in bh)
+        out = sorted((int(e), r) for r, e in enumerate(ho) if int(e) not in boot_hot)
+        back = sorted((int(e), r) for r, e in enumerate(co) if int(e) in boot_hot)
+        for (eh, r), (ec, b) in zip(out, back):
+            props.append(Swap(layer, r, b, eh, ec, 0.0))
+    return props if limit is None else props[:limit]
+
+
+class RuntimeControl:
+    """Applies a JSON control file to a policy when the file changes.
+
+    Keys (all optional): "freeze" (bool), "counting" (bool: whether the caller
+    passes the counter table to moe_route_split), any PolicyConfig budget
+    ("swaps_per_barrier", "swaps_per_layer", "min_avg", "hysteresis"),
+    "dump_counts" (a path: the next counter snapshot is written there as JSON)
+    and "restore_map" (true: queue a restore to the boot-time hot sets).
+    Unknown keys are reported, not applied."""
+
+    BUDGETS = ("swaps_per_barrier", "swaps_per_layer", "min_avg", "hysteresis")
+
+    def __init__(self, policy: AdaptivePolicy, path: str | None = None):
+        self.policy, self.path = policy, path
+        self.counting = True
+        self.restore_pending = False
+        self.dump_path = None
+        self._mtime = None
+
+    def apply(self, ctrl: dict) -> list:
+        """Apply one control record; returns the keys it did not know."""
+        unknown = []
+        names = {f.name for f in fields(PolicyConfig)}
+        for key, val in ctrl.items():
+            if key == "freeze":
+                self.policy.frozen = bool(val)
+            elif key == "counting":
+                self.counting = bool(val)
+            elif key == "restore_map":
+                self.restore_pending = bool(val)
+            elif key == "dump_counts":
+                self.dump_path = str(val) if val else None
+            elif key in self.BUDGETS and key in names:
+                cast = int if key.startswith("swaps") else float
+                setattr(self.policy.cfg, key, cast(val))
+            else:
+                unknown.append(key)
+        return unknown
+
+    def poll(self) -> list | None:
+        """Re-read the control file if it changed; returns the unknown keys of
+        the record applied, or None if nothing was read."""
+        if not self.path or not os.path.exists(self.path):
+            return None
+        mtime = os.stat(self.path).st_mtime_ns
+        if mtime == self._mtime:
+            return None
+        self._mtime = mtime
+        with open(self.path) as f:
+            return self.apply(json.load(f))
+
+    def maybe_dump(self, snapshot: np.ndarray) -> bool:
+        if not self.dump_path:
+            return False
+        with open(self.dump_path, "w") as f:
+            json.dump(np.asarray(snapshot).astype(np.int64).tolist(), f)
+        self.dump_path = None
+        return True
+
+
+class Telemetry:
+    """Appends one JSON object per line to a file (or keeps them in memory)."""
+
+    def __init__(self, path: str | None = None):
+        self.path = path
+        self.records = []
+
+    def log(self, **record) -> None:
+        self.records.append(record)
+        if self.path:
+            with open(self.path, "a") as f:
+                f.write(json.dumps(record) + "\n")
