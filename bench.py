@@ -81,6 +81,10 @@ def parse():
                     help="runtime control file (JSON) read at every policy barrier: freeze, "
                          "counting, budgets, dump_counts, restore_map")
     ap.add_argument("--telemetry", default=None, help="append one JSON line per policy barrier")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step (all its layer calls) as a HIP graph and replay it "
+                         "(workloads whose steps run every layer bank once: step40, offdomain, "
+                         "domainshift); per-kernel times are then not reported")
     return ap.parse_args()
 
 
@@ -280,8 +284,7 @@ def main():
         split = T * k * 4 + E * 4 + (T * k * 4) * 2
         return gu, gu + dn + cold_act + fin + split, uc * (b13 + b2), uh, uc, pc
 
-    def cold_ffn(c, l, timed):
-        xc = x_d[c % NX]
+    def cold_ffn(xc, l, timed):
         if timed:
             e = torch.cuda.Event(enable_timing=True)
             e.record(cold_s)
@@ -305,18 +308,20 @@ def main():
             e.record(main_s)
             ev["s1"].append(e)
 
-    def layer_call(c, timed):
+    def layer_call(c, timed, src=None):
         # hot_s runs the hot FFN, cold_s the cold path; the split and the
-        # finalize are on main_s, which is one of the two (or both, --serial)
+        # finalize are on main_s, which is one of the two (or both, --serial).
+        # src: (ids, weights, x) tensors to read instead of call c's own
+        # (the fixed buffers a captured graph reads)
         l = c % Lr
-        xc = x_d[c % NX]
-        moe.moe_route_split(ids_d[c], maps_dev[l], n_hot, n_cold, bufs.hot_split, bufs.cold_split,
+        ids_c, w_c, xc = src if src is not None else (ids_d[c], w_d[c], x_d[c % NX])
+        moe.moe_route_split(ids_c, maps_dev[l], n_hot, n_cold, bufs.hot_split, bufs.cold_split,
                             bufs.n_invalid, counts[l] if control.counting else None, 256,
                             stream=main_s)
         if cold_s is not main_s:
             # cold bank first on its own stream: its 8 workgroups start beside the hot bank's
             cold_s.wait_stream(main_s)
-            cold_ffn(c, l, timed)
+            cold_ffn(xc, l, timed)
         if hot_s is not main_s:
             hot_s.wait_stream(main_s)
         if timed:
@@ -336,12 +341,12 @@ def main():
             e.record(hot_s)
             ev["dn1"].append(e)
         if cold_s is main_s:
-            cold_ffn(c, l, timed)
+            cold_ffn(xc, l, timed)
         if hot_s is not main_s:
             main_s.wait_stream(hot_s)
         if cold_s is not main_s:
             main_s.wait_stream(cold_s)
-        moe.moe_finalize(bufs.Y, w_d[c], bufs.out, stream=main_s)
+        moe.moe_finalize(bufs.Y, w_c, bufs.out, stream=main_s)
 
     def apply_swaps(props):
         """Apply proposals between steps; returns (applied, refused as stale)."""
@@ -382,10 +387,51 @@ def main():
                       restoring=control.restore_pending,
                       **({"unknown_ctrl_keys": unknown} if unknown else {}))
 
+    graph = None
+    if args.graph:
+        # one captured graph per step: every layer call reads fixed input
+        # buffers, loaded before each replay; the banks, maps and counters it
+        # reads are the live ones (swaps between steps update them in place)
+        if lps % Lr:
+            sys.exit("--graph needs every step to run each layer bank once "
+                     "(layers per step a multiple of the rotated banks)")
+        ids_st = torch.empty((lps, T, k), dtype=torch.int32, device="cuda")
+        w_st = torch.empty((lps, T, k), dtype=torch.float32, device="cuda")
+        x_st = torch.empty((lps, T, H), dtype=torch.int16, device="cuda")
+        xsel = torch.tensor([[(s * lps + j) % NX for j in range(lps)] for s in range(S)],
+                            dtype=torch.int64, device="cuda")
+
+        def load_step(s):
+            ids_st.copy_(ids_d[s * lps:(s + 1) * lps], non_blocking=True)
+            w_st.copy_(w_d[s * lps:(s + 1) * lps], non_blocking=True)
+            torch.index_select(x_d, 0, xsel[s], out=x_st)
+
+        def static_step():
+            for j in range(lps):
+                layer_call(j, False, (ids_st[j], w_st[j], x_st[j]))
+
     with torch.cuda.stream(main_s):
         for s in range(args.warmup):
             step(s, False)
         torch.cuda.synchronize()
+        if args.graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=main_s):
+                static_step()
+            torch.cuda.synchronize()
+            log(f"captured one {lps}-layer step as a graph")
+
+            def step(s, timed):  # noqa: F811 (the graph replaces the eager step)
+                load_step(s)
+                if timed:
+                    e = torch.cuda.Event(enable_timing=True)
+                    e.record(main_s)
+                    ev["s0"].append(e)
+                graph.replay()
+                if timed:
+                    e = torch.cuda.Event(enable_timing=True)
+                    e.record(main_s)
+                    ev["s1"].append(e)
         t0 = time.perf_counter()
         windows, win_t, win_picks, win_cold, win_swaps = [], t0, 0, 0, 0
         for i in range(args.steps):
@@ -448,9 +494,13 @@ def main():
                                               for h, b in zip(hot_owner, boot_hot)),
                    "device_maps_equal_host": all(
                        np.array_equal(maps_dev[l].cpu().numpy(), maps_host[l]) for l in range(Lr))}
-    achieved = float(np.sum(hot_bytes_gu) / (gu_ms.sum() / 1e3) / 1e9)
+    # per-kernel events exist only for eager steps (not inside a replayed graph)
+    kern = len(gu_ms) > 0
+    mean_us = lambda v: round(float(v.mean() * 1e3), 1) if len(v) else None
+    achieved = float(np.sum(hot_bytes_gu) / (gu_ms.sum() / 1e3) / 1e9) if kern else None
     value = float(np.mean(bytes_step) / (ms_per_step / 1e3) / 1e9)
-    cold_link = float(np.sum(cold_bytes) / max(c_ms.sum() / 1e3, 1e-12) / 1e9)
+    cold_link = (float(np.sum(cold_bytes) / max(c_ms.sum() / 1e3, 1e-12) / 1e9)
+                 if len(c_ms) else None)
 
     # HBM traffic of the gate/up kernel from committed rocprofv3 counter runs,
     # used only while the kernel's sources are the ones the counters were taken on
@@ -482,14 +532,17 @@ def main():
                    "weights": "mxfp4", "cold_bank": COLD_BANK[args.cold_path], "map": args.map,
                    "layer_banks_rotated": Lr, "cold_stream": not args.serial,
                    "streams": "serial" if args.serial else args.streams,
+                   "graph": bool(args.graph),
                    "policy": not args.no_policy},
         "us_per_layer": round(ms_per_step * 1e3 / lps, 1),
         "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
-        "hot_gate_up_us": round(float(gu_ms.mean() * 1e3), 1),
-        "hot_down_us": round(float(dn_ms.mean() * 1e3), 1),
-        "cold_ffn_us": round(float(c_ms.mean() * 1e3), 1),
-        "hot_ffn_GBps": round(float((np.sum(uh_list) * (b13 + b2)) / ((gu_ms.sum() + dn_ms.sum()) / 1e3) / 1e9), 1),
-        "cold_link": {"achieved_GBps": round(cold_link, 1),
+        "hot_gate_up_us": mean_us(gu_ms),
+        "hot_down_us": mean_us(dn_ms),
+        "cold_ffn_us": mean_us(c_ms),
+        "hot_ffn_GBps": (round(float((np.sum(uh_list) * (b13 + b2)) /
+                                     ((gu_ms.sum() + dn_ms.sum()) / 1e3) / 1e9), 1) if kern
+                         else None),
+        "cold_link": {"achieved_GBps": round(cold_link, 1) if cold_link is not None else None,
                       "ceiling_GBps": ceilings.get("host_link_zero_copy_read_GBps"),
                       "nominal_GBps": NOMINAL_LINK_GBPS},
         "routing": {"hot_unique_per_step": round(float(np.mean(uh_list)), 2),
@@ -502,8 +555,10 @@ def main():
                                                         ("hot_down", dn_ms), ("cold_path", c_ms))},
         "ceilings": ceilings,
         "roofline": {"kernel": "ffn_gate_up_resident (hot bank)", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
+                     "achieved": round(achieved, 1) if kern else None, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4) if kern else None,
+                     "traffic": traffic},
     }
 
     if not args.no_cpu_baseline:
