@@ -28,6 +28,7 @@ steps of the same workload.
 from __future__ import annotations
 
 import argparse
+import bisect
 import ctypes
 import hashlib
 import json
@@ -284,29 +285,37 @@ def main():
         split = T * k * 4 + E * 4 + (T * k * 4) * 2
         return gu, gu + dn + cold_act + fin + split, uc * (b13 + b2), uh, uc, pc
 
+    # Everything the timed loop records or waits on is created beforehand, so
+    # the host work per step is the library calls themselves (the step must
+    # stay bound by the device, not by the host enqueueing it).
+    ev_pool = [torch.cuda.Event(enable_timing=True) for _ in range(7 * (args.steps + 4))]
+
+    def mark(name, stream):
+        e = ev_pool.pop()
+        e.record(stream)
+        ev[name].append(e)
+
+    fork_ev, join_hot_ev, join_cold_ev = torch.cuda.Event(), torch.cuda.Event(), torch.cuda.Event()
+
+    def wait(dst, src, e):  # dst waits for the work enqueued on src so far
+        e.record(src)
+        dst.wait_event(e)
+
     def cold_ffn(xc, l, timed):
         if timed:
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(cold_s)
-            ev["c0"].append(e)
+            mark("c0", cold_s)
         enqueue_cold_ffn(cold[l], bufs.cold_split, xc, k, H, I, bufs, stage, cold_s,
                          overlap=not args.serial)
         if timed:
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(cold_s)
-            ev["c1"].append(e)
+            mark("c1", cold_s)
 
     def step(s, timed):
         if timed:
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(main_s)
-            ev["s0"].append(e)
+            mark("s0", main_s)
         for j in range(lps):
             layer_call(s * lps + j, timed and j == 0)
         if timed:
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(main_s)
-            ev["s1"].append(e)
+            mark("s1", main_s)
 
     def layer_call(c, timed, src=None):
         # hot_s runs the hot FFN, cold_s the cold path; the split and the
@@ -320,32 +329,26 @@ def main():
                             stream=main_s)
         if cold_s is not main_s:
             # cold bank first on its own stream: its 8 workgroups start beside the hot bank's
-            cold_s.wait_stream(main_s)
+            wait(cold_s, main_s, fork_ev)
             cold_ffn(xc, l, timed)
         if hot_s is not main_s:
-            hot_s.wait_stream(main_s)
+            wait(hot_s, main_s, fork_ev)
         if timed:
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(hot_s)
-            ev["gu0"].append(e)
+            mark("gu0", hot_s)
         moe.moe_expert_gate_up_mxfp4(hot[l], bufs.hot_split, xc, k, I, bufs.workspace,
                                      stream=hot_s)
         if timed:
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(hot_s)
-            ev["gu1"].append(e)
+            mark("gu1", hot_s)
         moe.moe_expert_down_mxfp4(hot[l], bufs.hot_split, T, k, H, I, bufs.workspace, bufs.Y,
                                   stream=hot_s)
         if timed:
-            e = torch.cuda.Event(enable_timing=True)
-            e.record(hot_s)
-            ev["dn1"].append(e)
+            mark("dn1", hot_s)
         if cold_s is main_s:
             cold_ffn(xc, l, timed)
         if hot_s is not main_s:
-            main_s.wait_stream(hot_s)
+            wait(main_s, hot_s, join_hot_ev)
         if cold_s is not main_s:
-            main_s.wait_stream(cold_s)
+            wait(main_s, cold_s, join_cold_ev)
         moe.moe_finalize(bufs.Y, w_c, bufs.out, stream=main_s)
 
     def apply_swaps(props):
@@ -433,39 +436,54 @@ def main():
                     e.record(main_s)
                     ev["s1"].append(e)
         t0 = time.perf_counter()
-        windows, win_t, win_picks, win_cold, win_swaps = [], t0, 0, 0, 0
+        # the maps in force from each layer call on: the byte accounting runs
+        # after the timed loop, on the map each call saw
+        map_versions = [(0, [m.copy() for m in maps_host])]
+        host_us, marks, win_t, win_swaps = [], [], t0, 0
         for i in range(args.steps):
             s = args.warmup + i
-            step_bytes = 0
-            for j in range(lps):
-                c = s * lps + j
-                gu, tot, cb, uh, uc, pc = account(c, maps_host[c % Lr])
-                step_bytes += tot
-                if j == 0:
-                    hot_bytes_gu.append(gu)
-                    cold_bytes.append(cb)
-                uh_list.append(uh)
-                uc_list.append(uc)
-                cold_picks += pc
-                win_cold += pc
-                win_picks += T * k
-            bytes_step.append(step_bytes)
+            h0 = time.perf_counter()
             step(s, True)
+            host_us.append((time.perf_counter() - h0) * 1e6)
             if not args.no_policy and (s + 1) % policy.cfg.read_every == 0:
                 before = swaps
                 barrier(s + 1)
+                if swaps != before:
+                    map_versions.append(((s + 1) * lps, [m.copy() for m in maps_host]))
                 win_swaps += swaps - before
             if (off_domain or shift) and (i + 1) % 128 == 0:
                 torch.cuda.synchronize()
                 now = time.perf_counter()
-                windows.append({"steps": [i - 127, i + 1],
-                                **({"phase": "ABA"[phase_of(s * lps)]} if shift else {}),
-                                "cold_share_of_picks": round(win_cold / win_picks, 4),
-                                "us_per_layer": round((now - win_t) * 1e6 / (128 * lps), 1),
-                                "swaps_applied": win_swaps})
-                win_t, win_picks, win_cold, win_swaps = now, 0, 0, 0
+                marks.append((i, now - win_t, win_swaps))
+                win_t, win_swaps = now, 0
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+
+    starts = [v[0] for v in map_versions]
+    cold_by_step = []
+    for i in range(args.steps):
+        s = args.warmup + i
+        step_bytes = step_cold = 0
+        for j in range(lps):
+            c = s * lps + j
+            maps = map_versions[bisect.bisect_right(starts, c) - 1][1]
+            gu, tot, cb, uh, uc, pc = account(c, maps[c % Lr])
+            step_bytes += tot
+            if j == 0:
+                hot_bytes_gu.append(gu)
+                cold_bytes.append(cb)
+            uh_list.append(uh)
+            uc_list.append(uc)
+            cold_picks += pc
+            step_cold += pc
+        bytes_step.append(step_bytes)
+        cold_by_step.append(step_cold)
+    windows = [{"steps": [i - 127, i + 1],
+                **({"phase": "ABA"[phase_of((args.warmup + i) * lps)]} if shift else {}),
+                "cold_share_of_picks": round(sum(cold_by_step[i - 127:i + 1]) / (128 * lps * T * k),
+                                             4),
+                "us_per_layer": round(dt * 1e6 / (128 * lps), 1),
+                "swaps_applied": ws} for i, dt, ws in marks]
 
     K = args.steps
     ms_per_step = (t1 - t0) * 1e3 / K
@@ -553,6 +571,10 @@ def main():
         **({"restore": restore} if restore else {}),
         "percentiles_us": {name: pct(v) for name, v in (("step", st_ms), ("hot_gate_up", gu_ms),
                                                         ("hot_down", dn_ms), ("cold_path", c_ms))},
+        # host time to enqueue one step (no waiting): it must stay below the
+        # step's device time for the step to measure the device
+        "host_enqueue_us": {k: round(float(np.percentile(host_us, q)), 1)
+                            for k, q in (("p10", 10), ("p50", 50), ("p90", 90))},
         "ceilings": ceilings,
         "roofline": {"kernel": "ffn_gate_up_resident (hot bank)", "bound": "hbm",
                      "achieved": round(achieved, 1) if kern else None, "peak": PEAK_HBM_GBPS,

@@ -137,8 +137,14 @@ class Bank:
         return int(self.w13.shape[0])
 
     def abi(self) -> MoeBankC:
-        return MoeBankC(self.w13.data_ptr(), self.s13.data_ptr(), self.w2.data_ptr(),
-                        self.s2.data_ptr(), self.n_rows, 1 if self.on_host else 0)
+        # built once per set of tensors (the call path stays cheap on the host)
+        key = (id(self.w13), id(self.s13), id(self.w2), id(self.s2), self.on_host)
+        c = self.__dict__.get("_abi")
+        if c is None or c[0] != key:
+            c = (key, MoeBankC(self.w13.data_ptr(), self.s13.data_ptr(), self.w2.data_ptr(),
+                               self.s2.data_ptr(), self.n_rows, 1 if self.on_host else 0))
+            self.__dict__["_abi"] = c
+        return c[1]
 
     def tensors(self) -> dict:
         return {"w13": self.w13, "s13": self.s13, "w2": self.w2, "s2": self.s2}
@@ -162,8 +168,13 @@ class Split:
                    torch.zeros(max(T * k, 1), dtype=torch.int32, device=device))
 
     def abi(self) -> MoeSplitC:
-        return MoeSplitC(self.n_active.data_ptr(), self.active_rows.data_ptr(),
-                         self.row_off.data_ptr(), self.slots.data_ptr())
+        key = (id(self.n_active), id(self.active_rows), id(self.row_off), id(self.slots))
+        c = self.__dict__.get("_abi")
+        if c is None or c[0] != key:
+            c = (key, MoeSplitC(self.n_active.data_ptr(), self.active_rows.data_ptr(),
+                                self.row_off.data_ptr(), self.slots.data_ptr()))
+            self.__dict__["_abi"] = c
+        return c[1]
 
     def to_host(self):
         """(active_rows, row_off, slots) as numpy, trimmed to n_active."""

@@ -24,7 +24,10 @@
 //    some of its slots.
 //  - Each wavefront then streams its items' weight chunks back to back, kP
 //    ahead in a register ring, across item boundaries; only weight loads and
-//    one scale-block load per item go through the vector-memory queue.
+//    one scale-block load per item go through the vector-memory queue. Each
+//    chunk of a 16-row item is read as two whole-line loads (rows 0-7, rows
+//    8-15) and the halves are exchanged between partner lanes (see
+//    mxfp4_common.h).
 //  - An item's scale bytes (16 * kNG rows x I/32 bytes) are contiguous and
 //    16-byte aligned: the wavefront loads them with a few 16-byte loads when
 //    its prefetch enters the item, copies them into its own LDS slot when it
@@ -151,12 +154,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
     // Prefetch cursor: item, pass, chunk, this lane's weight row, and the
     // item's scale block.
     int p_pass = 0, p_c = 0, p_np = passes_of(p_it);
-    const uint8_t* pw;
+    const uint8_t* pw;  // the item's first row (whole-line loads add this lane's offsets)
     const uint8_t* psb;
     auto p_enter = [&](int it) {
       const int a = it / per, o0 = (it - a * per) * 16 * kNG;
       const size_t row = (uint32_t)__builtin_amdgcn_readfirstlane(active_rows[a]);
-      pw = w2 + (row * H + o0 + r) * wrb;
+      pw = w2 + (row * H + o0) * wrb;
       psb = s2 + (row * H + o0) * sbr;
     };
     p_enter(p_it);
@@ -181,22 +184,30 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
         p_enter(nx);
       }
     };
-    // Only the last chunk of the axis can have lanes past its end: they read
-    // the chunk's first block (in the same cache line as the lanes in range,
-    // where the row's first block would cost a second fetch of a line read
-    // long before); their scale is replaced by unit and their activations are
-    // the zero padding, so what they read does not change a bit of the result
-    // (finite E2M1 values times zero, accumulated from +0).
+    // Whole-line loads (line_load_a/_b): lane r's partner r^8 has the same q,
+    // so both are in range or both past the end of the axis. Only the last
+    // chunk can have lanes past its end: they read inside that chunk's first
+    // block (in the same cache line as the lanes in range); their scale is
+    // replaced by unit and their activations are the zero padding, so what
+    // they read does not change a bit of the result (finite E2M1 values times
+    // zero, accumulated from +0).
+    const bool upper = r >= 8;
     const bool lane_in_last = (nchunk - 1) * kChunkBlocks + 2 * q < nblk;
-    const int off_last = (nchunk - 1) * 128 + (lane_in_last ? 32 * q : 0);
-    // The scheduling barrier pins the loads at their place in the stream
-    // (left free, the compiler sinks them towards the end of a ring cycle,
-    // which shortens how far ahead they run).
+    const size_t off_a = line_load_a(r, q, wrb), off_b = line_load_b(r, q, wrb);
+    const size_t last_a = (nchunk - 1) * 128 + (lane_in_last ? off_a : off_a - 32 * q);
+    const size_t last_b = (nchunk - 1) * 128 + (lane_in_last ? off_b : off_b - 32 * q);
+    // Ordinary cache policy here: rows of I/2 bytes are not line-aligned, so
+    // a line holding the end of one chunk and the start of the next is read
+    // by two loads a chunk apart, and with the streaming policy it is gone by
+    // the second (measured: whole-line loads 115 -> 102 us per decode step
+    // with the ordinary policy, no gain with the streaming one). The
+    // scheduling barrier pins the loads at their place in the stream (left
+    // free, the compiler sinks them towards the end of a ring cycle, which
+    // shortens how far ahead they run).
     auto load_w = [&](AChunk& a) {
-      const int off = p_c == nchunk - 1 ? off_last : p_c * 128 + 32 * q;
-      const uint4* p = reinterpret_cast<const uint4*>(pw + off);
-      a.lo = p[0];
-      a.hi = p[1];
+      const bool last = p_c == nchunk - 1;
+      a.lo = *reinterpret_cast<const uint4*>(pw + (last ? last_a : p_c * 128 + off_a));
+      a.hi = *reinterpret_cast<const uint4*>(pw + (last ? last_b : p_c * 128 + off_b));
       __builtin_amdgcn_sched_barrier(0);
     };
     // The scale block of the cursor's item, kSbl granules per lane (separate
@@ -268,7 +279,7 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
               const bf16x8 bv =
                   *reinterpret_cast<const bf16x8*>(hs + lds_elem(lrow, kpad, e0 + 8 * m));
               acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  dequant8(word_of(ring[u], m), m < 4 ? s0 : s1), bv, acc, 0, 0, 0);
+                  dequant8(own_word(ring[u], m, upper), m < 4 ? s0 : s1), bv, acc, 0, 0, 0);
             }
           }
         }

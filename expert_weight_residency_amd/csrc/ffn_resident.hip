@@ -22,6 +22,11 @@
 //    weight chunks, issued unconditionally (past the wavefront's last chunk
 //    it re-reads its last 4 chunks, still in cache), so waiting for one chunk
 //    never waits for a newer one.
+//  - Each chunk of a 16-row group is read as two whole-line loads (rows 0-7,
+//    rows 8-15) with the streaming cache policy, and the halves are
+//    exchanged between partner lanes (see mxfp4_common.h): 163 -> 148 us
+//    alone per decode step against the two half-line loads of the operand
+//    layout (the gate/up rows of H/2 = 2048 bytes are line-aligned).
 //  - Scale bytes are loaded once per 4 chunks per row group (8 bytes per
 //    lane, one chunk's scales each) and redistributed across the lane
 //    quarters with two lane-swap instructions: a per-chunk 2-byte load per
@@ -51,12 +56,15 @@ size_t resident_lds_bytes(int T, int k, int H, int cap) {
          ((size_t)cap + (size_t)cap + 1 + 2 * (size_t)T * k) * sizeof(int32_t);
 }
 
-// This lane's 64 E2M1 codes of chunk c of a row (blocks 2q and 2q+1).
-__device__ __forceinline__ void load_w(AChunk& a, const uint8_t* __restrict__ wrow, int c, int q) {
-  const uint4* p = reinterpret_cast<const uint4*>(wrow + c * 128 + 32 * q);
-  a.lo = p[0];
-  a.hi = p[1];
+// Chunk c of a 16-row group as two whole-line loads (lo = load A, hi = load
+// B; see line_load_a/_b): pa, pb point at this lane's two offsets of chunk 0.
+__device__ __forceinline__ void load_w(AChunk& a, const uint8_t* __restrict__ pa,
+                                       const uint8_t* __restrict__ pb, int c) {
+  a.lo = ld_stream16(pa + c * 128);
+  a.hi = ld_stream16(pb + c * 128);
 }
+
+
 
 // Lane (r, q) holds raw = the 8 scale bytes of chunk c0 + q of its row r
 // (pair j = bytes 2j, 2j+1 belongs to lane quarter j). Transpose the 4 x 4
@@ -122,6 +130,7 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
   // scalar registers (values read from LDS would otherwise count as per-lane
   // and turn the loop into exec-masked control flow).
   const int lane = tid & 63, r = lane & 15, q = lane >> 4;
+  const bool upper = r >= 8;  // which of the two whole-line loads holds this lane's first half
   // The next item of the workgroup's run (g1 once none is left); one lane
   // takes it from the counter.
   auto take = [&]() {
@@ -145,16 +154,19 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
 
   // Prefetch cursor: item, pass, chunk, and this lane's two row pointers.
   int p_it = first, p_pass = 0, p_c = 0, p_npass = passes_of(first);
-  const uint8_t* pw[kNG];
+  const uint8_t* pa[kNG];  // this lane's whole-line load A / B of chunk 0, per group
+  const uint8_t* pb[kNG];
   const uint8_t* ps[kNG];
   auto p_rows = [&](int it) {
     const int a = it / per, i0 = (it - a * per) * 16;
     const size_t row = (uint32_t)__builtin_amdgcn_readfirstlane(l_rows[a]);
     const uint8_t* wexp = w13 + row * rows_per_expert * wrb;
     const uint8_t* sexp = s13 + row * rows_per_expert * srb;
-    pw[0] = wexp + (size_t)(i0 + r) * wrb;
+    pa[0] = wexp + (size_t)i0 * wrb + line_load_a(r, q, wrb);
+    pb[0] = wexp + (size_t)i0 * wrb + line_load_b(r, q, wrb);
     ps[0] = sexp + (size_t)(i0 + r) * srb;
-    pw[1] = wexp + (size_t)(I + i0 + r) * wrb;
+    pa[1] = wexp + (size_t)(I + i0) * wrb + line_load_a(r, q, wrb);
+    pb[1] = wexp + (size_t)(I + i0) * wrb + line_load_b(r, q, wrb);
     ps[1] = sexp + (size_t)(I + i0 + r) * srb;
   };
   p_rows(p_it);
@@ -194,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
 #pragma unroll
   for (int p = 0; p < P; ++p) {
 #pragma unroll
-    for (int g = 0; g < kNG; ++g) load_w(ring[p][g], pw[g], p_c, q);
+    for (int g = 0; g < kNG; ++g) load_w(ring[p][g], pa[g], pb[g], p_c);
     p_advance();
   }
 
@@ -219,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
         for (int u = 0; u <= P; ++u) {
           const int cc = c + u;
 #pragma unroll
-          for (int g = 0; g < kNG; ++g) load_w(ring[(u + P) % (P + 1)][g], pw[g], p_c, q);
+          for (int g = 0; g < kNG; ++g) load_w(ring[(u + P) % (P + 1)][g], pa[g], pb[g], p_c);
           p_advance();
           if (u == 0) {
             // the cursor now stands at the first chunk of the next quad
@@ -242,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
 #pragma unroll
             for (int g = 0; g < kNG; ++g)
               acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  dequant8(word_of(ring[u][g], m), sc[g][m >> 2]), bv, acc[g], 0, 0, 0);
+                  dequant8(own_word(ring[u][g], m, upper), sc[g][m >> 2]), bv, acc[g], 0, 0, 0);
           }
         }
       }

@@ -12,6 +12,43 @@ namespace mx {
 constexpr int kChunkElems = 256;  // reduction elements per chunk per row
 constexpr int kChunkBlocks = 8;   // E8M0 blocks per chunk
 
+// Weight loads over whole 128-byte lines. In the MFMA operand layout lane
+// (r, q) needs bytes 32q .. 32q+31 of chunk c of row r; two 16-byte loads of
+// that layout would each touch 16 rows x half a line. Instead, for one group
+// of 16 rows: load A reads rows 0-7 whole (lane r < 8: bytes 32q .. +15 of
+// row r, its own; lane r >= 8: bytes 32q+16 .. +31 of row r-8, its partner's)
+// and load B rows 8-15 (lane r >= 8: its own first half of row r; lane r < 8:
+// the second half of row r+8). Each load is then 8 full lines, which the
+// memory system streams faster, also with the streaming cache policy. After
+// arrival, lo_word / hi_word give the dwords of the lane's own 32 bytes: the
+// first half is in A or B, the second half is in partner lane r^8's other
+// load, fetched with a DPP row rotation by 8 (bank-masked: lanes 0-7 of a
+// row take lane r+8's A, lanes 8-15 take lane r-8's B). The bytes each lane
+// ends with are exactly those of the row-per-lane loads.
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Byte offsets, from the group's first row, of this lane's two loads.
+__device__ __forceinline__ size_t line_load_a(int r, int q, size_t row_bytes) {
+  return (size_t)(r & 7) * row_bytes + 32 * q + (r >= 8 ? 16 : 0);
+}
+__device__ __forceinline__ size_t line_load_b(int r, int q, size_t row_bytes) {
+  return (size_t)(8 + (r & 7)) * row_bytes + 32 * q + (r < 8 ? 16 : 0);
+}
+
+constexpr int kDppRowRor8 = 0x128;  // DPP row_ror:8 (lane r of a row reads lane (r+8) mod 16)
+
+__device__ __forceinline__ uint32_t lo_word(uint32_t a, uint32_t b, bool upper) {
+  return upper ? b : a;
+}
+__device__ __forceinline__ uint32_t hi_word(uint32_t a, uint32_t b) {
+  const int t = __builtin_amdgcn_update_dpp(0, (int)a, kDppRowRor8, 0xf, 0x3, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(t, (int)b, kDppRowRor8, 0xf, 0xc, false);
+}
+
 struct AChunk {
   uint4 lo, hi;  // 64 E2M1 codes of one row: blocks 2q and 2q+1 of the chunk
   uint16_t sc;   // their two E8M0 scale bytes (widened where used)
@@ -46,6 +83,13 @@ __device__ __forceinline__ uint32_t word_of(const AChunk& a, int m) {
     case 2: return v.z;
     default: return v.w;
   }
+}
+
+// Word m (0..7) of this lane's own 32 bytes of a chunk held as the two
+// whole-line loads A (in lo) and B (in hi); upper: r >= 8.
+__device__ __forceinline__ uint32_t own_word(const AChunk& a, int m, bool upper) {
+  const uint32_t wa = word_of(a, m & 3), wb = word_of(a, 4 + (m & 3));
+  return m < 4 ? lo_word(wa, wb, upper) : hi_word(wa, wb);
 }
 
 // 8 E2M1 codes (one dword, low nibble first) times a power-of-two scale -> 8 bf16.

@@ -52,8 +52,12 @@ class ColdStage:
         t = {k: torch.empty(sh, dtype=torch.uint8, device=device) for k, sh in shapes.items()}
         self.bank = Bank(t["w13"], t["s13"], t["w2"], t["s2"], on_host=False)
         self.rows = torch.zeros(max(n_rows, 1), dtype=torch.int32, device=device)
-        # runs the FFN on the stage while the copy is still going (see ResidencyLayer)
+        # runs the FFN on the stage while the copy is still going (see
+        # enqueue_cold_ffn), with the two events that order it (re-recorded
+        # every call: a wait takes the record before it)
         self.ffn_stream = torch.cuda.Stream(device=device)
+        self.gu_ready = torch.cuda.Event()
+        self.gu_done = torch.cuda.Event()
 
 
 def enqueue_cold_ffn(cold: Bank, split: Split, x, k: int, H: int, I: int, bufs: LayerBuffers,
@@ -76,16 +80,14 @@ def enqueue_cold_ffn(cold: Bank, split: Split, x, k: int, H: int, I: int, bufs: 
         return stream
     staged = moe_stage_rows(cold, split, T, k, stage.bank, stage.rows, H, I,
                             parts=STAGE_GATE_UP, stream=stream)
-    gu_ready = torch.cuda.Event()
-    gu_ready.record(stream)
+    stage.gu_ready.record(stream)
     moe_stage_rows(cold, split, T, k, stage.bank, stage.rows, H, I, parts=STAGE_DOWN,
                    stream=stream)
     f = stage.ffn_stream
-    f.wait_event(gu_ready)
+    f.wait_event(stage.gu_ready)
     moe_expert_gate_up_mxfp4(stage.bank, staged, x, k, I, bufs.workspace, stream=f)
-    gu_done = torch.cuda.Event()
-    gu_done.record(f)
-    stream.wait_event(gu_done)
+    stage.gu_done.record(f)
+    stream.wait_event(stage.gu_done)
     moe_expert_down_mxfp4(stage.bank, staged, T, k, H, I, bufs.workspace, bufs.Y, stream=stream)
     return stream
 
