@@ -1,7 +1,8 @@
 """GPU parity at the full expert shapes: 384 experts, top-6, H=4096, I=2880,
 295 hot rows in HBM and 89 cold rows in pinned host memory read in place.
-Decode (16 tokens) is checked on every slot; the 4096-token prefill chunk on
-sampled slots and tokens."""
+Decode (16 and 7 tokens) is checked on every slot; 112 tokens with the
+positional map (staged == in place bitwise) and the 4096-token prefill chunk
+on sampled slots and tokens."""
 import numpy as np
 import pytest
 import torch
@@ -91,6 +92,67 @@ def test_decode_split_equals_all_hot_at_full_shape(banks):
     torch.cuda.empty_cache()
     assert np.array_equal(Ys, Yu)
     assert np.array_equal(outs, outu)
+
+
+def test_decode_T7_every_slot(banks):
+    """One layer call of the 40-layer step (7 tokens: a verify window)."""
+    rm, ho, co, hot, cold = banks
+    ids, w = synth.skewed_routing(7, K, E, SEED, 0, 3)
+    x = synth.activations(7, H, SEED, step=3)
+    Y, out, ninv = run_layer(hot, cold, rm, ids, w, x, H, I)
+    assert ninv == 0
+    Yr, outr = _oracle_for(ids, w, x)
+    e_y, e_o = rel_errors(Y, Yr.reshape(-1, H)), rel_errors(out, outr)
+    log(f"T=7: Y {e_y}  out {e_o}")
+    assert e_y[0] <= REL_L2 and e_y[1] <= MAX_REL
+    assert e_o[0] <= REL_L2 and e_o[1] <= MAX_REL
+    for s in range(7 * K):
+        assert rel_errors(Y[s], Yr.reshape(-1, H)[s])[0] <= REL_L2, s
+
+
+def test_decode_T112_positional_map_staged(banks):
+    """High-concurrency step (112 tokens) with the positional map (the last 89
+    ids cold, ~23% of picks): the decode gate/up family (T > 16) and the
+    persistent down kernel; the cold path staged into HBM on a side stream
+    gives the bits of the in-place cold path; sampled tokens (incl. cold
+    picks) against the oracle."""
+    _, ho, co, hot, cold = banks
+    T = 112
+    rm, ho_p, co_p = synth.positional_map(E, 89)
+    # the fixture's banks hold the fitted map's rows: refill for the positional one
+    hot_p = empty_bank_host(len(ho_p), H, I, device="cuda")
+    synth.fill_bank_device(hot_p.tensors(), torch.from_numpy(ho_p).cuda(), SEED, 0, H, I)
+    cold_p = empty_bank_host(len(co_p), H, I, pinned=True)
+    synth.fill_bank_host(cold_p.tensors(), co_p, SEED, 0, H, I)
+    ids, w = synth.skewed_routing(T, K, E, SEED, 0, 11)
+    x = synth.activations(T, H, SEED, step=11)
+    n_cold_picks = int((rm[ids] < 0).sum())
+    log(f"T=112 positional: {n_cold_picks} cold picks, "
+        f"{len(np.unique(ids[rm[ids] < 0]))} cold experts")
+    assert n_cold_picks > 0
+    Y0, o0, ninv = run_layer(hot_p, cold_p, rm, ids, w, x, H, I)
+    assert ninv == 0
+    from expert_weight_residency_amd.layer import ColdStage, LayerBuffers, ResidencyLayer
+    from gpu_util import routing_tensors
+    ids_d, w_d, x_d = routing_tensors(ids, w, x)
+    bufs = LayerBuffers.allocate(T, K, H, I, hot_p.n_rows, cold_p.n_rows)
+    layer = ResidencyLayer(hot_p, cold_p, torch.from_numpy(rm).cuda(), H, I,
+                           stage=ColdStage(min(89, T * K), H, I))
+    layer.forward(x_d, ids_d, w_d, bufs, hot_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    Y1 = bufs.Y[: T * K].cpu().numpy().view(np.uint16)
+    o1 = bufs.out[:T].cpu().numpy().view(np.uint16)
+    assert np.array_equal(Y0, Y1) and np.array_equal(o0, o1)
+    t_cold = np.nonzero((rm[ids] < 0).any(axis=1))[0]
+    tokens = np.unique(np.concatenate([t_cold[:4], [0, 57, T - 1]]))
+    Yr, outr = _oracle_for(ids, w, x, tokens)
+    e_y = rel_errors(Y0.reshape(T, K, H)[tokens], Yr)
+    e_o = rel_errors(o0[tokens], outr)
+    log(f"  sampled {len(tokens)} tokens: Y {e_y} out {e_o}")
+    assert e_y[0] <= REL_L2 and e_y[1] <= MAX_REL
+    assert e_o[0] <= REL_L2 and e_o[1] <= MAX_REL
+    del hot_p, cold_p
+    torch.cuda.empty_cache()
 
 
 def test_prefill_T4096_sampled(banks):
