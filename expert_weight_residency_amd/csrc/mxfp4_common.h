@@ -1,7 +1,8 @@
-// MXFP4 operand helpers shared by the two expert-FFN kernel families (decode
-// and token-tiled). Both take the reduction axis in the same 256-element
-// chunks and the same lane-to-element assignment, and run the same MFMA
-// sequence per output element, so a pick gives the same bits from either.
+// MXFP4 operand helpers shared by the expert-FFN kernels (resident gate/up,
+// persistent down, decode and token-tiled). All take the reduction axis in the
+// same 256-element chunks and the same lane-to-element assignment, and run the
+// same MFMA sequence per output element, so a pick gives the same bits from
+// any of them.
 #pragma once
 
 #include "internal.h"
@@ -51,6 +52,8 @@ __device__ __forceinline__ uint32_t hi_word(uint32_t a, uint32_t b) {
 
 struct AChunk {
   uint4 lo, hi;  // 64 E2M1 codes of one row: blocks 2q and 2q+1 of the chunk
+                 // (kernels with whole-line loads keep loads A and B here; own_word
+                 // turns them into these codes)
   uint16_t sc;   // their two E8M0 scale bytes (widened where used)
 };
 
