@@ -514,6 +514,7 @@ def main():
                        np.array_equal(maps_dev[l].cpu().numpy(), maps_host[l]) for l in range(Lr))}
     # per-kernel events exist only for eager steps (not inside a replayed graph)
     kern = len(gu_ms) > 0
+    has_cold = np.array([b > 0 for b in cold_bytes[-len(gu_ms):]], bool) if kern else None
     mean_us = lambda v: round(float(v.mean() * 1e3), 1) if len(v) else None
     achieved = float(np.sum(hot_bytes_gu) / (gu_ms.sum() / 1e3) / 1e9) if kern else None
     value = float(np.mean(bytes_step) / (ms_per_step / 1e3) / 1e9)
@@ -555,6 +556,9 @@ def main():
         "us_per_layer": round(ms_per_step * 1e3 / lps, 1),
         "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
         "hot_gate_up_us": mean_us(gu_ms),
+        # the same launches split by whether the step staged cold rows beside them
+        "hot_gate_up_us_by_step": ({"without_cold": mean_us(gu_ms[~has_cold]),
+                                    "with_cold": mean_us(gu_ms[has_cold])} if kern else None),
         "hot_down_us": mean_us(dn_ms),
         "cold_ffn_us": mean_us(c_ms),
         "hot_ffn_GBps": (round(float((np.sum(uh_list) * (b13 + b2)) /

@@ -299,10 +299,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
   }
 }
 
-// Rows of h one workgroup can stage, at most `want`.
+// Rows of h one workgroup can stage, at most `want` (the kernel's static LDS,
+// the item counter, is kept out of the dynamic allocation's budget).
+constexpr size_t kStaticLds = 256;
 int rows_that_fit(const Shape& s, int want) {
   const size_t dev = device_lds_per_block();
-  const size_t lim = dev < kLdsMax ? dev : kLdsMax;
+  const size_t lim = (dev < kLdsMax ? dev : kLdsMax) - kStaticLds;
   const size_t fixed = (size_t)kWaves * s.sbw;
   if (fixed >= lim) return 0;
   const size_t per_row = (size_t)s.kpad * 2 + 4;

@@ -107,20 +107,39 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
   const int g1 = min(n, g0 + qb);
   __shared__ int l_next;  // next item of the workgroup's run not yet taken
   {
-    const int gpr = kpad / 8;
-    for (int gi = tid; gi < T * gpr; gi += kThreads) {
-      const int n = gi / gpr, g = gi - n * gpr;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (g * 8 < H) v = *reinterpret_cast<const uint4*>(x + (size_t)n * H + g * 8);
-      *reinterpret_cast<uint4*>(xs + lds_elem(n, kpad, g * 8)) = v;
+    // Every thread issues all of its staging loads before its first LDS
+    // store, so the workgroup waits for about one round trip to memory
+    // instead of one per loop step. Loads and stores are unconditional: a
+    // thread past the end of a table copies the table's last entry again (the
+    // same value its owner writes), so no load sits under a branch. Slot
+    // entries past the split's count are copied too (the slot list has T*k
+    // entries); nothing reads them. na >= 1 here (the run is not empty).
+    constexpr int kB = 8;  // granules of x per thread per batch
+    const int gpr = kpad / 8, ng = T * gpr;
+    for (int i0 = 0; i0 <= na || i0 < picks; i0 += kThreads) {
+      const int i = i0 + tid;
+      const int ir = i < na ? i : na - 1, io = i <= na ? i : na, is = i < picks ? i : picks - 1;
+      const int vr = active_rows[ir], vo = row_off[io], vs = slots[is];
+      l_rows[ir] = vr;
+      l_off[io] = vo;
+      l_slot[is] = vs;
+      l_tok[is] = vs / k;
     }
-    for (int i = tid; i < na; i += kThreads) l_rows[i] = active_rows[i];
-    for (int i = tid; i <= na; i += kThreads) l_off[i] = row_off[i];
-    const int nslots = na > 0 ? row_off[na] : 0;
-    for (int i = tid; i < nslots && i < picks; i += kThreads) {
-      const int sl = slots[i];
-      l_slot[i] = sl;
-      l_tok[i] = sl / k;
+    for (int b0 = 0; b0 < ng; b0 += kB * kThreads) {
+      uint4 v[kB];
+      int dst[kB];
+      uint32_t pad = 0;  // bit u: granule u is zero padding past H
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+        const int gi = min(b0 + u * kThreads + tid, ng - 1);
+        const int n = gi / gpr, g = gi - n * gpr;
+        v[u] = *reinterpret_cast<const uint4*>(x + (size_t)n * H + (g * 8 < H ? g * 8 : 0));
+        pad |= (g * 8 >= H ? 1u : 0u) << u;
+        dst[u] = lds_elem(n, kpad, g * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        *reinterpret_cast<uint4*>(xs + dst[u]) = (pad >> u) & 1u ? make_uint4(0, 0, 0, 0) : v[u];
     }
     if (tid == 0) l_next = g0;
   }
