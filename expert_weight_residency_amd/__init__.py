@@ -61,7 +61,7 @@ def lib():
         L.moe_expert_bytes.restype = sz
         L.moe_expert_bytes.argtypes = [i32, i32]
         L.moe_ffn_workspace_bytes.restype = sz
-        L.moe_ffn_workspace_bytes.argtypes = [i32, i32, i32]
+        L.moe_ffn_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
         L.moe_route_split.restype = i32
@@ -115,8 +115,8 @@ def moe_expert_bytes(H: int, I: int) -> int:
     return int(lib().moe_expert_bytes(H, I))
 
 
-def moe_ffn_workspace_bytes(T: int, k: int, I: int) -> int:
-    return int(lib().moe_ffn_workspace_bytes(T, k, I))
+def moe_ffn_workspace_bytes(T: int, k: int, H: int, I: int) -> int:
+    return int(lib().moe_ffn_workspace_bytes(T, k, H, I))
 
 
 # ------------------------------------------------------------ containers --

@@ -77,8 +77,9 @@ size_t moe_expert_bytes(int H, int I) {
          (size_t)H * (I / 32);
 }
 
-size_t moe_ffn_workspace_bytes(int T, int k, int I) {
-  if (T <= 0 || k <= 0 || I <= 0) return 0;
+size_t moe_ffn_workspace_bytes(int T, int k, int H, int I) {
+  if (T <= 0 || k <= 0 || H <= 0 || I <= 0) return 0;
+  if (moe::ffn_use_fp4(T)) return moe::ffn_fp4_workspace_bytes(T, k, H, I);
   return (size_t)T * k * I * sizeof(uint16_t);
 }
 

@@ -271,6 +271,8 @@ int ffn_max_reduction() { return kLdsTile / (int)sizeof(uint16_t); }
 hipError_t launch_gate_up(const uint8_t* w13, const uint8_t* s13, int cap, int on_host,
                           const moe_split& sp, const uint16_t* x, int T, int k, int H, int I,
                           uint16_t* h_ws, hipStream_t stream) {
+  if (ffn_use_fp4(T))
+    return launch_gate_up_fp4(w13, s13, cap, on_host, sp, x, T, k, H, I, h_ws, stream);
   if (ffn_use_resident(T, k, H, cap, s13))
     return launch_gate_up_resident(w13, s13, cap, on_host, sp, x, T, k, H, I, h_ws, stream);
   if (ffn_use_tiled(T, k, cap))
@@ -288,6 +290,8 @@ hipError_t launch_gate_up(const uint8_t* w13, const uint8_t* s13, int cap, int o
 hipError_t launch_down(const uint8_t* w2, const uint8_t* s2, int cap, int on_host,
                        const moe_split& sp, int T, int k, int H, int I, const uint16_t* h_ws,
                        uint16_t* Y, hipStream_t stream) {
+  if (ffn_use_fp4(T))
+    return launch_down_fp4(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
   if (ffn_use_tiled(T, k, cap))
     return launch_down_tiled(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
   if (ffn_use_down_resident(T, k, H, I, s2))

@@ -32,11 +32,13 @@
 
 #include "internal.h"
 #include "mxfp4_common.h"
+#include "tile_items.h"
 
 namespace moe {
 namespace {
 
 using namespace mx;
+using namespace tiles;
 
 constexpr int kTok = 64;                         // tokens per tile
 constexpr int kTokGroups = kTok / 16;            // MFMA column groups per tile
@@ -50,47 +52,6 @@ constexpr int kStage = kTok * kGranules / kThreads;  // granules staged per thre
 constexpr int kXcds = 8;
 static_assert(kStage * kThreads == kTok * kGranules, "staging must cover the tile");
 static_assert(kThreads / kGranules * kStage == kTok, "staging rows");
-
-// Exclusive prefix over the active rows of their tile counts, into tpre[0..na].
-__device__ void build_tile_prefix(const int32_t* __restrict__ row_off, int na, int* tpre,
-                                  int* wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int carry = 0;
-  for (int base = 0; base < na; base += kThreads) {
-    const int a = base + tid;
-    const int v = a < na ? (row_off[a + 1] - row_off[a] + kTok - 1) / kTok : 0;
-    int s = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(s, d, 64);
-      if (lane >= d) s += o;
-    }
-    if (lane == 63) wsum[wv] = s;
-    __syncthreads();
-    int before = 0, total = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-      before += i < wv ? wsum[i] : 0;
-      total += wsum[i];
-    }
-    if (a < na) tpre[a] = carry + before + s - v;
-    carry += total;
-    __syncthreads();
-  }
-  if (tid == 0) tpre[na] = carry;
-  __syncthreads();
-}
-
-// Active row holding tile `tile` (every active row has at least one tile).
-__device__ __forceinline__ int row_of_tile(const int* tpre, int na, int tile) {
-  int lo = 0, hi = na - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tpre[mid] <= tile) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
 
 // kGateUp: gate/up GEMM + SwiGLU (src = x rows by token, dst = h by slot).
 // Otherwise: down GEMM (src = h rows by slot, dst = Y by slot).
@@ -115,7 +76,7 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_tiled(
   const int r = lane & 15, q = lane >> 4;
 
   const int na = *n_active;
-  build_tile_prefix(row_off, na, tpre, wsum);
+  build_tile_prefix<kTok, kWaves>(row_off, na, tpre, wsum);
   const int items = tpre[na] * blocks_per_tile;
 
   // Workgroup b runs on XCD b % 8 (dispatch is round-robin over the XCDs):

@@ -83,6 +83,21 @@ constexpr int kTiledMinPicksPerRow = 16;
 constexpr int kTiledHostWaves = 64;
 bool ffn_use_tiled(int T, int k, int cap);
 
+// Steps of at least kFp4MinTokens tokens (prefill) run both GEMMs on the
+// block-scaled FP4 matrix instruction (ffn_fp4.hip), for every bank: the choice
+// depends on the step only, so split and unsplit steps take the same path.
+// Its activations travel as two E4M3 terms per bf16 value, in the workspace
+// (ffn_fp4_workspace_bytes).
+constexpr int kFp4MinTokens = MOE_FP4_MIN_TOKENS;
+bool ffn_use_fp4(int T);
+size_t ffn_fp4_workspace_bytes(int T, int k, int H, int I);
+hipError_t launch_gate_up_fp4(const uint8_t* w13, const uint8_t* s13, int cap, int on_host,
+                              const moe_split& split, const uint16_t* x, int T, int k, int H,
+                              int I, void* ws, hipStream_t stream);
+hipError_t launch_down_fp4(const uint8_t* w2, const uint8_t* s2, int cap, int on_host,
+                           const moe_split& split, int T, int k, int H, int I, const void* ws,
+                           uint16_t* Y, hipStream_t stream);
+
 // Copy split.active_rows[a] of the four src tensors to row a of dst, and
 // dst_rows[a] = a, for a < *split.n_active (stage_rows.hip).
 hipError_t launch_stage_rows(const uint8_t* const src[4], uint8_t* const dst[4],

@@ -33,7 +33,7 @@ class LayerBuffers:
 
     @classmethod
     def allocate(cls, T: int, k: int, H: int, I: int, n_hot: int, n_cold: int, device="cuda"):
-        ws = max(moe_ffn_workspace_bytes(T, k, I), 16)
+        ws = max(moe_ffn_workspace_bytes(T, k, H, I), 16)
         return cls(Split.empty(n_hot, T, k, device), Split.empty(n_cold, T, k, device),
                    torch.zeros(1, dtype=torch.int32, device=device),
                    torch.empty(ws, dtype=torch.uint8, device=device),

@@ -64,6 +64,9 @@ extern "C" {
 #define MOE_MAX_EXPERTS 4096
 #define MOE_MAX_ROWS 4096
 #define MOE_MAX_TOPK 32
+/* Steps of at least this many tokens (prefill) run the expert FFN on the
+ * block-scaled FP4 matrix instruction; see moe_expert_ffn_mxfp4. */
+#define MOE_FP4_MIN_TOKENS 256
 
 /* One residency bank. The four pointers are device-accessible: device memory
  * for the hot bank; for the cold bank, pinned host memory (hipHostMalloc or
@@ -96,10 +99,13 @@ typedef struct moe_split {
 /* Bytes of one expert row (all four tensors) at hidden H, intermediate I. */
 size_t moe_expert_bytes(int H, int I);
 
-/* Bytes of the device workspace moe_expert_ffn_mxfp4 needs: the bf16 SwiGLU
- * output h [T*k][I]. Both bank calls of one layer may share one workspace:
- * each writes only its own slots. */
-size_t moe_ffn_workspace_bytes(int T, int k, int I);
+/* Bytes of the device workspace moe_expert_ffn_mxfp4 needs at step size T:
+ * below MOE_FP4_MIN_TOKENS tokens, the bf16 SwiGLU output h [T*k][I]; from
+ * MOE_FP4_MIN_TOKENS on, x and h per slot as the two E4M3 terms the FP4 path
+ * reads ((T*k) * (ceil(H/256) + ceil(I/256)) * 528 bytes). Both bank calls of
+ * one layer may share one workspace: each writes only its own slots. 0 when
+ * any argument is <= 0. */
+size_t moe_ffn_workspace_bytes(int T, int k, int H, int I);
 
 /*
  * moe_route_split -- residency split with deterministic compaction and the
@@ -144,10 +150,17 @@ int moe_route_split(const int32_t *topk_ids, int T, int k, const int32_t *row_ma
  *
  * The per-(row, slot) arithmetic, including its reduction order, does not
  * depend on the bank, the row index, the other slots or the grid, so a pick
- * gives the same bits from either bank.
+ * gives the same bits from either bank. It depends on the step size only:
+ * below MOE_FP4_MIN_TOKENS tokens the weights are dequantized to bf16 (exact)
+ * for bf16 matrix products; from MOE_FP4_MIN_TOKENS on (prefill) the E2M1
+ * weights and their scales go to the block-scaled FP4 matrix instruction as
+ * stored, with each bf16 activation (x, and h after its bf16 rounding) carried
+ * as two E4M3 terms with E8M0 per-32 scales, which hold it to within 2^-9 of
+ * its magnitude ("vLLM: Pin Hot Experts": the MXFP4 expert GEMM; the FP4
+ * instruction where the token count makes the GEMM a dense contraction).
  *
  * bank: see moe_bank. split: this bank's moe_route_split output (device).
- * x: device bf16 [T][H]. workspace: device, moe_ffn_workspace_bytes(T,k,I)
+ * x: device bf16 [T][H]. workspace: device, moe_ffn_workspace_bytes(T,k,H,I)
  * bytes. Y: device bf16 [T*k][H]. Launches two kernels (gate/up + SwiGLU,
  * then down); launches nothing when T == 0 or the bank has no rows.
  */

@@ -38,8 +38,12 @@ def test_exports_every_declared_symbol(L):
 def test_sizes(L):
     assert moe.moe_expert_bytes(4096, 2880) == 18_800_640
     assert moe.moe_expert_bytes(256, 128) == 52_224
-    assert moe.moe_ffn_workspace_bytes(16, 6, 2880) == 16 * 6 * 2880 * 2
-    assert moe.moe_ffn_workspace_bytes(0, 6, 2880) == 0
+    assert moe.moe_ffn_workspace_bytes(16, 6, 4096, 2880) == 16 * 6 * 2880 * 2
+    assert moe.moe_ffn_workspace_bytes(255, 6, 4096, 2880) == 255 * 6 * 2880 * 2
+    # prefill-sized steps: x and h per slot as two E4M3 terms (512 data + 16 scale
+    # bytes per 256-element chunk; H = 4096 -> 16 chunks, I = 2880 -> 12)
+    assert moe.moe_ffn_workspace_bytes(256, 6, 4096, 2880) == 256 * 6 * (16 + 12) * 528
+    assert moe.moe_ffn_workspace_bytes(0, 6, 4096, 2880) == 0
 
 
 def _split(p=0x1000):

@@ -275,7 +275,7 @@ def test_stage_calls_equal_fused_call():
     hs, cs = moe.Split.empty(len(ho), T, k), moe.Split.empty(len(co), T, k)
     ninv = torch.zeros(1, dtype=torch.int32, device="cuda")
     moe.moe_route_split(ids_d, rm_d, len(ho), len(co), hs, cs, ninv)
-    ws = torch.empty(moe.moe_ffn_workspace_bytes(T, k, I), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(moe.moe_ffn_workspace_bytes(T, k, H, I), dtype=torch.uint8, device="cuda")
     Y1 = torch.zeros((T * k, H), dtype=torch.int16, device="cuda")
     Y2 = torch.zeros((T * k, H), dtype=torch.int16, device="cuda")
     moe.moe_expert_ffn_mxfp4(bank, hs, x_d, k, I, ws, Y1)
