@@ -627,7 +627,8 @@ def run_prefill(args):
     """One 4096-token prefill chunk of the full layer per step: split (counter
     off: more than 256 tokens), hot FFN on the main stream, cold FFN on a side
     stream, finalize. The hot bank runs the FP4-instruction kernels; their MFMA
-    utilisation is reported against the dense bf16 peak, and its HBM rate
+    utilisation is reported against half the dense fp8 peak (two terms per
+    activation), and their HBM rate
     against 8 TB/s."""
     import torch
 

@@ -31,9 +31,14 @@
 // (These operand placements were measured on the device with one-hot and
 // random operands; they are what the instruction computes, not a choice.)
 //
-// Work items, tiles, XCD-aware order and the double-buffered LDS staging
-// follow ffn_tiled.hip: item = (tile of up to 64 slots of one expert, block of
-// weight rows), 8 wavefronts each own 64 weight rows x the tile's 64 tokens.
+// Work items, tiles and the XCD-aware order follow ffn_tiled.hip: item =
+// (tile of up to 64 slots of one expert, block of weight rows), 8 wavefronts
+// each own 64 weight rows x the tile's 64 tokens. The tile's quantized
+// activation chunks reach LDS by 16-byte global-to-LDS copies into two static
+// buffers (no registers held across the chunk's arithmetic), each step naming
+// its buffer at compile time so that the compiler need not wait for the copy
+// into one buffer before reading the other; the barrier between steps waits
+// for the copy only, not for the weight loads issued after it.
 // The gate/up epilogue applies SwiGLU, rounds h to bf16 exactly as the other
 // families do, and writes it already split into the two terms for the down
 // kernel. Per output element the accumulation order (chunks in order; per
@@ -57,15 +62,50 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kTok = 64;                 // tokens per tile
 constexpr int kTokGroups = kTok / 16;    // MFMA column groups per tile
-constexpr int kWaves = 8;                // wavefronts per workgroup
+constexpr int kWaves = 8;                // wavefronts per workgroup (two per SIMD)
 constexpr int kThreads = 64 * kWaves;
+constexpr int kWavesPerSimd = kWaves / 4;  // register budget: 256 per wavefront
 constexpr int kGroups = 4;               // 16-row MFMA groups per wavefront
 constexpr int kP = 1;                    // weight chunks in flight per wavefront
+// Steps per unrolled cycle: a whole number of ring turns and of the two LDS
+// buffers, so each step's ring slot and buffer are compile-time constants.
+constexpr int kCycle = (kP + 1) % 2 == 0 ? kP + 1 : 2 * (kP + 1);
 constexpr int kQData = 512;              // quantized data bytes per row per chunk (hi, lo)
 constexpr int kQScale = 16;              // quantized scale bytes per row per chunk
-constexpr int kBufBytes = kTok * (kQData + kQScale);  // one LDS activation buffer
 constexpr int kXcds = 8;
 constexpr int kFmtFp4 = 4, kFmtFp8 = 0;  // the instruction's operand format codes
+constexpr int kLoadsPerChunk = 3 * kGroups;  // a chunk of weights: per group 2 x 16 B + scales
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wavefront are outstanding (other counters untouched).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// ... and also until all of this wavefront's LDS reads have returned.
+constexpr int vmcnt_lds_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+
+// Workgroup barrier after an explicit wait (waitcnt immediate W), with an
+// acquire fence after it so no later memory access moves above it, and
+// scheduling barriers so nothing moves across the wait.
+#define wg_barrier(W)                                   \
+  do {                                                  \
+    __builtin_amdgcn_sched_barrier(0);                  \
+    __builtin_amdgcn_s_waitcnt(W);                      \
+    __builtin_amdgcn_s_barrier();                       \
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup"); \
+    __builtin_amdgcn_sched_barrier(0);                  \
+  } while (0)
+// Chunk c of this lane's weight row in group g: the group's first row at
+// `gb` (wave-uniform), this lane's row at gb + lw, its scales at sb + ls.
+// As load_a: past the end of the axis the lane reads block 0 (in bounds).
+__device__ __forceinline__ void load_w(AChunk& a, const uint8_t* __restrict__ gb,
+                                       const uint8_t* __restrict__ sb, uint32_t lw, uint32_t ls,
+                                       int c, int q, int nblk) {
+  const int b0 = c * kChunkBlocks + 2 * q;
+  const uint32_t bb = b0 < nblk ? (uint32_t)b0 : 0u;
+  const uint4* p = reinterpret_cast<const uint4*>(gb + (lw + 16u * bb));
+  a.lo = p[0];
+  a.hi = p[1];
+  a.sc = *reinterpret_cast<const uint16_t*>(sb + (ls + bb));
+}
 
 // ---- the two-term E4M3 split ----------------------------------------------
 
@@ -177,13 +217,15 @@ __global__ __launch_bounds__(256) void quant_x_slots(
 }
 
 // The B operand of one (token group T, MFMA J) step: both terms (8 dwords
-// each) and the scale dword, from the LDS buffer `bd`.
+// each) from the LDS data buffer `bd` and the scale dword from the LDS scale
+// buffer `bs`.
 struct BFrag {
   v8i h, l;
   int sc;
 };
 template <int T, int J>
-__device__ __forceinline__ BFrag load_b(const unsigned char* bd, int r, int q) {
+__device__ __forceinline__ BFrag load_b(const unsigned char* bd, const unsigned char* bs, int r,
+                                        int q) {
   const int n = 16 * T + r;
   const unsigned char* rowp = bd + n * kQData;
   const int g0 = 2 * (4 * J + q);  // first granule of this lane's 32 bytes of a term
@@ -194,7 +236,7 @@ __device__ __forceinline__ BFrag load_b(const unsigned char* bd, int r, int q) {
   BFrag b;
   b.h = v8i{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
   b.l = v8i{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
-  b.sc = *reinterpret_cast<const int*>(bd + kTok * kQData + n * kQScale + 4 * q);
+  b.sc = *reinterpret_cast<const int*>(bs + n * kQScale + 4 * q);
   return b;
 }
 
@@ -207,10 +249,11 @@ __device__ __forceinline__ BFrag load_b(const unsigned char* bd, int r, int q) {
 template <int S, int NT>
 __device__ __forceinline__ void chunk_steps(f32x4 (&acc)[kGroups][kTokGroups],
                                             const AChunk (&a)[kGroups], const int (&sca)[kGroups],
-                                            const unsigned char* bd, int r, int q, const BFrag& cur) {
+                                            const unsigned char* bd, const unsigned char* bs,
+                                            int r, int q, const BFrag& cur) {
   constexpr int T = S / 2, J = S % 2;
   BFrag nxt;
-  if constexpr (S + 1 < 2 * NT) nxt = load_b<(S + 1) / 2, (S + 1) % 2>(bd, r, q);
+  if constexpr (S + 1 < 2 * NT) nxt = load_b<(S + 1) / 2, (S + 1) % 2>(bd, bs, r, q);
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
     const uint4 a4 = J ? a[g].hi : a[g].lo;
@@ -226,7 +269,16 @@ __device__ __forceinline__ void chunk_steps(f32x4 (&acc)[kGroups][kTokGroups],
         av, cur.l, acc[g][T], kFmtFp4, kFmtFp8, J, sca[g], 2 + J, cur.sc);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (S + 1 < 2 * NT) chunk_steps<S + 1, NT>(acc, a, sca, bd, r, q, nxt);
+  if constexpr (S + 1 < 2 * NT) chunk_steps<S + 1, NT>(acc, a, sca, bd, bs, r, q, nxt);
+}
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // ---- the GEMM ---------------------------------------------------------------
@@ -235,16 +287,23 @@ __device__ __forceinline__ void chunk_steps(f32x4 (&acc)[kGroups][kTokGroups],
 // split into two terms by slot). Otherwise: down GEMM (B = quantized h rows by
 // slot, output = Y bf16 by slot).
 template <bool kGateUp>
-__global__ __launch_bounds__(kThreads, 2) void ffn_fp4(
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void ffn_fp4(
     const uint8_t* __restrict__ w, const uint8_t* __restrict__ s,
     const int32_t* __restrict__ n_active, const int32_t* __restrict__ active_rows,
     const int32_t* __restrict__ row_off, const int32_t* __restrict__ slots,
     const uint8_t* __restrict__ bq_d, const uint8_t* __restrict__ bq_s, int H, int I,
     int blocks_per_tile, uint8_t* __restrict__ hq_d, uint8_t* __restrict__ hq_s,
     uint16_t* __restrict__ Y) {
+  // Two activation buffers as separate objects: with the ring unrolled by an
+  // even count, every access names one of them statically, so the compiler
+  // can tell a copy into one buffer from reads of the other and need not
+  // wait for the copy before those reads.
+  __shared__ __align__(16) unsigned char buf0[kTok * kQData];
+  __shared__ __align__(16) unsigned char buf1[kTok * kQData];
+  __shared__ __align__(16) unsigned char sbuf0[kTok * kQScale];
+  __shared__ __align__(16) unsigned char sbuf1[kTok * kQScale];
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* bufs = smem;                                        // [2][kBufBytes]
-  int* tpre = reinterpret_cast<int*>(smem + 2 * kBufBytes);          // [na + 1]
+  int* tpre = reinterpret_cast<int*>(smem);                          // [na + 1]
   __shared__ int wsum[kWaves];
 
   const int K = kGateUp ? H : I;       // reduction length
@@ -253,8 +312,10 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_fp4(
   const int nch_out = (I + kChunkElems - 1) / kChunkElems;  // chunks of an h row
   const size_t wrb = K / 2, srb = K / 32;
   const size_t rows_per_expert = kGateUp ? 2 * (size_t)I : (size_t)H;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r = lane & 15, q = lane >> 4;
+  const uint32_t lw = (uint32_t)r * (uint32_t)wrb, ls = (uint32_t)r * (uint32_t)srb;
 
   const int na = *n_active;
   build_tile_prefix<kTok, kWaves>(row_off, na, tpre, wsum);
@@ -284,48 +345,56 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_fp4(
     const size_t row = active_rows[a];
     const uint8_t* wexp = w + row * rows_per_expert * wrb;
     const uint8_t* sexp = s + row * rows_per_expert * srb;
-    const uint8_t* wrow[kGroups];
-    const uint8_t* srow[kGroups];
+    // first row of each group (wave-uniform); a lane adds r rows
+    const uint8_t* wgb[kGroups];
+    const uint8_t* sgb[kGroups];
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
       size_t wr;
-      if (kGateUp) wr = (g < 2 ? 0 : (size_t)I) + c0 + 16 * (g & 1) + r;
-      else wr = (size_t)c0 + 16 * g + r;
-      if (!busy) wr = r;
-      wrow[g] = wexp + wr * wrb;
-      srow[g] = sexp + wr * srb;
+      if (kGateUp) wr = (g < 2 ? 0 : (size_t)I) + c0 + 16 * (g & 1);
+      else wr = (size_t)c0 + 16 * g;
+      if (!busy) wr = 0;
+      wgb[g] = wexp + wr * wrb;
+      sgb[g] = sexp + wr * srb;
     }
 
     // Staging of one chunk of the tile's quantized rows straight into LDS
     // (16-byte global-to-LDS loads: lane L of a wavefront's load lands at
     // granule L of the wavefront's 1 KB destination, from any address). Load
-    // u of wavefront w fills LDS granules p = (8u + w) * 64 + L: row
-    // n = 16u + 2w + L/32, stored granule L%32, which holds the row's granule
-    // (L%32) ^ (n & 7) (the read side's bank swizzle). Wavefront 0 also loads
-    // the 64 scale granules. Rows past the tile's last slot read its first
-    // slot: their token columns compute garbage that is never written out
-    // (the MFMA's output columns are independent).
-    const uint8_t* src_row[4];
+    // u of wavefront w fills LDS granules p = (kWaves*u + w) * 64 + L: row
+    // n = p / 32, stored granule L%32, which holds the row's granule
+    // (L%32) ^ (n & 7) (the read side's bank swizzle); every wavefront also
+    // copies the 64 scale granules (the same bytes to the same place). The
+    // copies are unconditional, so the compiler sees each one followed by
+    // exactly one chunk of weight loads: rows past the tile's last slot copy
+    // its first slot (their token columns compute values that are never
+    // written out: the MFMA's output columns are independent), and the chunk
+    // index is clamped. (Byte offsets stay below 4 GB: the rows of T*k slots.)
+    constexpr int kU = kTok * 32 / kThreads;  // copies per wavefront per chunk
+    uint32_t src_row[kU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int n = 16 * u + 2 * wv + (lane >> 5);
-      const int sl = slots[t0 + (n < nvalid ? n : 0)];
-      src_row[u] = bq_d + (size_t)(uint32_t)sl * nchunk * kQData + 16 * ((lane & 31) ^ (n & 7));
+    for (int u = 0; u < kU; ++u) {
+      const int n = 2 * (kWaves * u + wv) + (lane >> 5);
+      const uint32_t sl = (uint32_t)slots[t0 + (n < nvalid ? n : 0)];
+      src_row[u] = sl * (uint32_t)(nchunk * kQData) + 16u * (uint32_t)((lane & 31) ^ (n & 7));
     }
-    const uint8_t* src_sc =
-        bq_s + (size_t)(uint32_t)slots[t0 + (lane < nvalid ? lane : 0)] * nchunk * kQScale;
-    auto stage = [&](int c, int buf) {
-      unsigned char* bd = bufs + buf * kBufBytes;
+    const uint32_t src_sc =
+        (uint32_t)slots[t0 + (lane < nvalid ? lane : 0)] * (uint32_t)(nchunk * kQScale);
+    // stage(integral_constant<int, b>, c): chunk c into buffer b (named
+    // statically, so each copy targets one of the two objects)
+    auto stage = [&](auto bufc, int c) __attribute__((always_inline)) {
+      const uint32_t cc = (uint32_t)(c < nchunk ? c : nchunk - 1);
+      unsigned char* bd = decltype(bufc)::value ? buf1 : buf0;
+      unsigned char* bs = decltype(bufc)::value ? sbuf1 : sbuf0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        __builtin_amdgcn_global_load_lds(src_row[u] + (size_t)c * kQData,
-                                         bd + (8 * u + wv) * 64 * 16, 16, 0, 0);
-      if (wv == 0)
-        __builtin_amdgcn_global_load_lds(src_sc + (size_t)c * kQScale, bd + kTok * kQData, 16, 0,
-                                         0);
+      for (int u = 0; u < kU; ++u)
+        __builtin_amdgcn_global_load_lds(bq_d + (src_row[u] + cc * kQData),
+                                         bd + (kWaves * u + wv) * 64 * 16, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bq_s + (src_sc + cc * kQScale), bs, 16, 0, 0);
+      // keep the copies ahead of the weight loads issued next: the waits
+      // below count those loads to know the copies are done
+      __builtin_amdgcn_sched_barrier(0);
     };
-    // all of this wavefront's global loads (its LDS copies among them) done
-    auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0); };
 
     f32x4 acc[kGroups][kTokGroups];
 #pragma unroll
@@ -333,58 +402,66 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_fp4(
 #pragma unroll
       for (int t = 0; t < kTokGroups; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto run = [&](auto ntc) {
+    using B0 = std::integral_constant<int, 0>;
+    auto run = [&](auto ntc) __attribute__((always_inline)) {
       constexpr int NT = decltype(ntc)::value;
       AChunk ring[kP + 1][kGroups];
-      stage(0, 0);
+      stage(B0{}, 0);
 #pragma unroll
       for (int p = 0; p < kP; ++p)
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) load_a(ring[p][g], wrow[g], srow[g], p, q, nblk);
-      wait_loads();
-      __syncthreads();
-      for (int c = 0; c < nchunk; c += kP + 1) {
-#pragma unroll
-        for (int u = 0; u <= kP; ++u) {
+        for (int g = 0; g < kGroups; ++g) load_w(ring[p][g], wgb[g], sgb[g], lw, ls, p, q, nblk);
+      // the copy of chunk 0 is done once at most the kP chunks of weight
+      // loads issued after it are outstanding
+      wg_barrier(vmcnt_lds_imm(kP * kLoadsPerChunk));
+      for (int c = 0; c < nchunk; c += kCycle) {
+        // step u of this cycle is chunk c + u; c is a multiple of the cycle,
+        // so chunk c + u is in ring slot u % (kP + 1) and LDS buffer u & 1
+        static_for<0, kCycle>([&](auto uc) __attribute__((always_inline)) {
+          constexpr int u = decltype(uc)::value;
           const int cc = c + u;
-          if (cc >= nchunk) break;
-          // the buffer filled here was last read in chunk cc - 1, which every
-          // wavefront finished before the last barrier
-          if (cc + 1 < nchunk) stage(cc + 1, (cc + 1) & 1);
+          // Copies, weight loads and the wait run for every step of the cycle
+          // (past the last chunk they re-read clamped, in-bounds data), so the
+          // compiler counts exactly one chunk of weight loads after each copy;
+          // only the arithmetic is skipped past the last chunk.
+          // The buffer filled here was last read in chunk cc - 1, which every
+          // wavefront finished before the last barrier.
+          stage(std::integral_constant<int, (u + 1) & 1>{}, cc + 1);
 #pragma unroll
           for (int g = 0; g < kGroups; ++g)
-            load_a(ring[(u + kP) % (kP + 1)][g], wrow[g], srow[g], cc + kP, q, nblk);
-          // a lane past the end of the axis has weight block 0 in its
-          // registers: unit scales (the activations there are zero)
-          const bool ok = cc * kChunkBlocks + 2 * q < nblk;
-          int sca[kGroups];
+            load_w(ring[(u + kP) % (kP + 1)][g], wgb[g], sgb[g], lw, ls, cc + kP, q, nblk);
+          constexpr int slot = u % (kP + 1);
+          if (busy && cc < nchunk) {
+            // a lane past the end of the axis has weight block 0 in its
+            // registers: unit scales (the activations there are zero)
+            const bool ok = cc * kChunkBlocks + 2 * q < nblk;
+            int sca[kGroups];
 #pragma unroll
-          for (int g = 0; g < kGroups; ++g) sca[g] = ok ? (int)ring[u][g].sc : 0x7f7f;
-          const unsigned char* bd = bufs + (cc & 1) * kBufBytes;
-          chunk_steps<0, NT>(acc, ring[u], sca, bd, r, q, load_b<0, 0>(bd, r, q));
-          wait_loads();
-          __syncthreads();
-        }
+            for (int g = 0; g < kGroups; ++g) sca[g] = ok ? (int)ring[slot][g].sc : 0x7f7f;
+            const unsigned char* bd = (u & 1) ? buf1 : buf0;
+            const unsigned char* bs = (u & 1) ? sbuf1 : sbuf0;
+            chunk_steps<0, NT>(acc, ring[slot], sca, bd, bs, r, q, load_b<0, 0>(bd, bs, r, q));
+          }
+          // The copy of chunk cc + 1 is done once at most the one chunk of
+          // weight loads issued after it is outstanding, and this buffer's
+          // reads are done once the LDS counter is zero; then the barrier
+          // hands both buffers over. (No release fence before it: that would
+          // also wait for the weight loads, and the only LDS writes in the
+          // loop are these copies, complete by the wait. The acquire fence
+          // after it keeps the next step's LDS reads below it.)
+          wg_barrier(vmcnt_lds_imm(kLoadsPerChunk));
+        });
       }
     };
 
-    if (busy) {
-      switch (ntg) {
-        case 1: run(std::integral_constant<int, 1>{}); break;
-        case 2: run(std::integral_constant<int, 2>{}); break;
-        case 3: run(std::integral_constant<int, 3>{}); break;
-        default: run(std::integral_constant<int, 4>{}); break;
-      }
-    } else {
-      // A wavefront past the last weight row only helps stage.
-      stage(0, 0);
-      wait_loads();
-      __syncthreads();
-      for (int cc = 0; cc < nchunk; ++cc) {
-        if (cc + 1 < nchunk) stage(cc + 1, (cc + 1) & 1);
-        wait_loads();
-        __syncthreads();
-      }
+    // Every wavefront runs the same steps (copies, weight loads, waits and
+    // barriers); one past the last weight row loads rows of group 0 and
+    // skips the arithmetic.
+    switch (ntg) {
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      default: run(std::integral_constant<int, 4>{}); break;
     }
 
     // Epilogue: lane (r, q) holds rows 4q + v of each group for token 16t + r.
@@ -471,7 +548,8 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_fp4(
   }
 }
 
-size_t fp4_lds_bytes(int cap) { return 2 * (size_t)kBufBytes + ((size_t)cap + 1) * sizeof(int); }
+// Dynamic LDS of a launch: the tile prefix (the two activation buffers are static).
+size_t fp4_lds_bytes(int cap) { return ((size_t)cap + 1) * sizeof(int); }
 
 // Workgroups for a launch (items are grid-strided): one per CU less the CUs a
 // concurrent host-bank launch holds for a device bank; kHostBankCUs for a bank
@@ -519,7 +597,9 @@ hipError_t launch_gate_up_fp4(const uint8_t* w13, const uint8_t* s13, int cap, i
                      nH, r.xq_d, r.xq_s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int blocks = (I + kChunkElems - 1) / kChunkElems;  // 8 waves x 32 i-columns
+  // wavefronts of 32 i-columns, up to the end of I's last chunk (the
+  // wavefronts past I write that chunk's zero blocks)
+  const int blocks = (I + kChunkElems - 1) / kChunkElems * (kChunkElems / 32) / kWaves;
   hipLaunchKernelGGL(ffn_fp4<true>, dim3(fp4_grid(cap, T, k, blocks, on_host)), dim3(kThreads),
                      fp4_lds_bytes(cap), stream, w13, s13, sp.n_active, sp.active_rows,
                      sp.row_off, sp.slots, r.xq_d, r.xq_s, H, I, blocks, r.hq_d, r.hq_s,
