@@ -2,9 +2,11 @@
 //
 // Same operation as the decode kernels in ffn_mxfp4.hip (gate/up GEMM +
 // SwiGLU into h, then the down GEMM into unweighted bf16 rows of Y; "vLLM: Pin
-// Hot Experts", section "Results, September 17"), organised for prefill-sized
-// steps where an expert has tens to hundreds of tokens ("We Built the
-// Counter", section 7: prefill wants larger tiles than decode's 8 tokens).
+// Hot Experts", section "Results, September 17"), organised for calls where
+// an expert has tens of tokens ("We Built the Counter", section 7: bigger
+// steps want larger tiles than decode's 8 tokens). It runs below 256 tokens
+// per step, when a bank averages 16 or more picks per row; from 256 tokens
+// (prefill) the FP4 kernels of ffn_fp4.hip take over.
 //
 //  - Work item = (tile of up to 64 of one expert's slots, block of 512 weight
 //    rows). A workgroup of 8 wavefronts runs one item; each wavefront owns 64
