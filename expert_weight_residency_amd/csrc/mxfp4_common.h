@@ -2,8 +2,8 @@
 // gate/up, persistent down, decode and token-tiled). All take the reduction
 // axis in the same 256-element chunks and the same lane-to-element assignment,
 // and run the same MFMA sequence per output element, so a pick gives the same
-// bits from any of them. (The FP4 kernels of ffn_fp4.hip use load_a and the
-// chunk constants too; their arithmetic is their own.)
+// bits from any of them. (The FP4 kernels of ffn_fp4.hip share the chunk
+// constants and AChunk; their arithmetic is their own.)
 #pragma once
 
 #include "internal.h"
