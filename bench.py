@@ -78,6 +78,12 @@ def parse():
                          "moving experts, reported in windows; domainshift: 7 tokens, traffic "
                          "from the map's ranking, then another, then the first again (equal "
                          "phases), the policy following, then a restore to the boot map")
+    ap.add_argument("--routing", default="auto", choices=["auto", "independent", "window"],
+                    help="independent: every token routed on its own (skewed per-expert "
+                         "probabilities); window: tokens in verify windows of 7 share a "
+                         "per-window term, fitted to the pages' touched-set curve; auto: window "
+                         "for the 7-token workloads and highconc (16 windows of 7), independent "
+                         "for decode and prefill")
     ap.add_argument("--ctrl", default=None,
                     help="runtime control file (JSON) read at every policy barrier: freeze, "
                          "counting, budgets, dump_counts, restore_map")
@@ -195,6 +201,10 @@ def main():
         args.steps, args.warmup = 1536, min(args.warmup, 8)
         wname = f"domain_shift_a_b_a_decode_t7_{args.layers}_layers"
     E, k, H, I, T = 384, 6, 4096, 2880, args.tokens
+    routing = args.routing
+    if routing == "auto":
+        routing = "window" if args.workload in ("step40", "highconc", "offdomain",
+                                                 "domainshift") else "independent"
     n_cold = 89
     n_hot = E - n_cold
     Lr, seed = args.layers, args.seed
@@ -249,7 +259,10 @@ def main():
     x_np = np.empty((NX, T, H), np.uint16)
     for c in range(C):
         pm = perms_b[c % Lr] if shift and phase_of(c) == 1 else perms[c % Lr]
-        ids_np[c], w_np[c] = synth.skewed_routing(T, k, E, seed, c % Lr, c, perm=pm)
+        if routing == "window":
+            ids_np[c], w_np[c] = synth.window_routing(T, k, E, seed, c % Lr, c, perm=pm)
+        else:
+            ids_np[c], w_np[c] = synth.skewed_routing(T, k, E, seed, c % Lr, c, perm=pm)
     for c in range(NX):
         x_np[c] = synth.activations(T, H, seed, c % Lr, c)
     ids_d = torch.from_numpy(ids_np).cuda()
@@ -547,6 +560,7 @@ def main():
                    "hidden": H, "layers_per_step": lps,
                    "traffic": ("off-domain" if off_domain else
                                "domain shift A-B-A" if shift else "in-domain"),
+                   "routing": ("verify windows of 7" if routing == "window" else "independent"),
                    "intermediate": I, "tokens": T, "hot_rows": n_hot, "cold_rows": n_cold,
                    "weights": "mxfp4", "cold_bank": COLD_BANK[args.cold_path], "map": args.map,
                    "layer_banks_rotated": Lr, "cold_stream": not args.serial,

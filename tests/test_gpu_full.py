@@ -94,16 +94,20 @@ def test_decode_split_equals_all_hot_at_full_shape(banks):
     assert np.array_equal(outs, outu)
 
 
-def test_decode_T7_every_slot(banks):
-    """One layer call of the 40-layer step (7 tokens: a verify window)."""
+@pytest.mark.parametrize("routing", ["independent", "window"])
+def test_decode_T7_every_slot(banks, routing):
+    """One layer call of the 40-layer step (7 tokens: a verify window), with
+    tokens routed independently or correlated within the window (fewer
+    distinct experts, more tokens per expert)."""
     rm, ho, co, hot, cold = banks
-    ids, w = synth.skewed_routing(7, K, E, SEED, 0, 3)
+    gen = synth.window_routing if routing == "window" else synth.skewed_routing
+    ids, w = gen(7, K, E, SEED, 0, 3)
     x = synth.activations(7, H, SEED, step=3)
     Y, out, ninv = run_layer(hot, cold, rm, ids, w, x, H, I)
     assert ninv == 0
     Yr, outr = _oracle_for(ids, w, x)
     e_y, e_o = rel_errors(Y, Yr.reshape(-1, H)), rel_errors(out, outr)
-    log(f"T=7: Y {e_y}  out {e_o}")
+    log(f"T=7 {routing}: {len(np.unique(ids))} experts, Y {e_y}  out {e_o}")
     assert e_y[0] <= REL_L2 and e_y[1] <= MAX_REL
     assert e_o[0] <= REL_L2 and e_o[1] <= MAX_REL
     for s in range(7 * K):

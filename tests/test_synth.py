@@ -77,6 +77,38 @@ def test_routing_skew_matches_pages(golden_dir):
     assert abs(np.mean(pos) - np.mean(shares[:3])) < 0.02   # sampling agrees with the pmf
 
 
+def test_verify_window_routing_matches_pages(golden_dir):
+    """The verify-window generator touches as many experts per window as the
+    pages measured (within 6%), independent tokens touch far more, and its
+    pick distribution keeps the decode skew (Gini, fitted cold share)."""
+    g = json.load(open(os.path.join(golden_dir, "verify_window_touched_set.json")))
+    skew = json.load(open(os.path.join(golden_dir, "routing_skew.json")))
+    E, k = 384, g["top_k"]
+    want = {int(w): v for w, v in g["unique_experts_by_window_tokens"].items()}
+    for w, v in want.items():
+        got = np.mean([len(np.unique(synth.window_routing(w, k, E, 3, 0, step, window=w)[0]))
+                       for step in range(400)])
+        assert abs(got - v) <= 0.06 * v, (w, got, v)
+        if w >= 4:  # independent tokens: at least 25% more
+            iid = np.mean([len(np.unique(synth.skewed_routing(w, k, E, 3, 0, step)[0]))
+                           for step in range(200)])
+            assert iid > 1.25 * v, (w, iid)
+    rm, _, _ = synth.fitted_map(E, 89, 3, 0)
+    cnt, cold = np.zeros(E), []
+    for step in range(300):
+        ids, wts = synth.window_routing(112, k, E, 3, 0, step)
+        cnt += np.bincount(ids.ravel(), minlength=E)
+        cold.append((rm[ids] < 0).mean())
+        assert ids.shape == (112, k) and np.allclose(wts.sum(axis=1), 1, atol=1e-6)
+        assert all(len(set(r)) == k for r in ids)  # distinct picks per token
+    assert abs(synth.gini(cnt) - skew["mean_gini"]) < 0.04
+    lo, hi = skew["fitted_cold_share_range"]
+    assert lo <= np.mean(cold) <= hi
+    a, _ = synth.window_routing(14, k, E, 3, 0, 5)
+    b, _ = synth.window_routing(14, k, E, 3, 0, 5)
+    assert np.array_equal(a, b)  # deterministic
+
+
 def test_maps_are_bijections():
     for rm, ho, co in (synth.fitted_map(384, 89, 1, 0), synth.positional_map(384, 89),
                        synth.random_map(16, 4, 3), synth.all_hot_map(8)):
