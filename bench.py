@@ -69,7 +69,7 @@ def parse():
                          "the cold FFN reads the pinned host bank directly")
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "step40", "highconc", "offdomain",
-                             "domainshift"],
+                             "domainshift", "refit"],
                     help="decode: the default line (one layer of 16 tokens per step); prefill: "
                          "one 4096-token chunk per step (counter off), with the hot bank's MFMA "
                          "utilisation; step40: 40 layer calls of 7 tokens per step; highconc: "
@@ -77,7 +77,13 @@ def parse():
                          "map fitted to one ranking, traffic from another, the adaptive policy "
                          "moving experts, reported in windows; domainshift: 7 tokens, traffic "
                          "from the map's ranking, then another, then the first again (equal "
-                         "phases), the policy following, then a restore to the boot map")
+                         "phases), the policy following, then a restore to the boot map; refit: "
+                         "the off-domain boot, a count-only profile (--profile-tokens per layer), "
+                         "a map fitted off-line to those counts and applied, then timed on fresh "
+                         "traffic with no on-line policy")
+    ap.add_argument("--profile-tokens", type=int, default=50_000,
+                    help="refit: decode tokens counted per layer before fitting (the pages' "
+                         "floor for a count profile is 50,000)")
     ap.add_argument("--routing", default="auto", choices=["auto", "independent", "window"],
                     help="independent: every token routed on its own (skewed per-expert "
                          "probabilities); window: tokens in verify windows of 7 share a "
@@ -173,14 +179,15 @@ def main():
     import expert_weight_residency_amd as moe
     import synth
     from expert_weight_residency_amd.layer import ColdStage, LayerBuffers, enqueue_cold_ffn
+    from expert_weight_residency_amd import mapfit
     from expert_weight_residency_amd.policy import (AdaptivePolicy, RuntimeControl, Telemetry,
-                                                    restore_swaps)
+                                                    restore_swaps, swaps_to)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.lib()
     if args.workload == "prefill":
         return run_prefill(args)
-    lps, off_domain, shift, wname = 1, False, False, None
+    lps, off_domain, shift, refit, wname = 1, False, False, False, None
     if args.workload == "step40":
         args.tokens, lps = 7, 40
         args.steps, args.warmup = min(args.steps, 32), min(args.warmup, 4)
@@ -200,11 +207,18 @@ def main():
         args.tokens, shift, lps = 7, True, args.layers
         args.steps, args.warmup = 1536, min(args.warmup, 8)
         wname = f"domain_shift_a_b_a_decode_t7_{args.layers}_layers"
+    elif args.workload == "refit":
+        # the off-domain boot, re-profiled and re-fitted off-line ("vLLM: Pin Hot
+        # Experts", the count-only boot and the evening's off-line re-profile)
+        args.tokens, off_domain, refit, lps = 7, True, True, args.layers
+        args.steps, args.warmup = min(args.steps, 256), min(args.warmup, 8)
+        args.no_policy = True
+        wname = f"refit_off_domain_decode_t7_{args.layers}_layers"
     E, k, H, I, T = 384, 6, 4096, 2880, args.tokens
     routing = args.routing
     if routing == "auto":
         routing = "window" if args.workload in ("step40", "highconc", "offdomain",
-                                                 "domainshift") else "independent"
+                                                 "domainshift", "refit") else "independent"
     n_cold = 89
     n_hot = E - n_cold
     Lr, seed = args.layers, args.seed
@@ -242,7 +256,11 @@ def main():
     # --- per-call inputs, generated and uploaded before timing ---------------
     # call c = step * lps + j runs on layer bank c % Lr; its routing follows that
     # bank's ranking (or, off-domain, an independent ranking of the same shape)
-    S = args.warmup + args.steps
+    # steps [0, prof): the count-only profile (refit); [prof, base): warm-up;
+    # [base, S): timed
+    prof = -(-args.profile_tokens // args.tokens) if refit else 0
+    base = prof + args.warmup
+    S = base + args.steps
     C = S * lps
     perms = [synth.layer_permutation(E, seed ^ 0x0FFD0 if off_domain else seed, l)
              for l in range(Lr)]
@@ -250,7 +268,7 @@ def main():
     phase_len = args.steps // 3
 
     def phase_of(c):  # domain-shift phase of layer call c: 0 (A), 1 (B), 2 (A)
-        i = c // lps - args.warmup
+        i = c // lps - base
         return 0 if i < phase_len else (1 if i < 2 * phase_len else 2)
 
     ids_np = np.empty((C, T, k), np.int32)
@@ -403,6 +421,61 @@ def main():
                       restoring=control.restore_pending,
                       **({"unknown_ctrl_keys": unknown} if unknown else {}))
 
+    def profile_and_refit():
+        """Count-only profile over steps [0, prof) on the boot map (counter on,
+        no swaps; snapshots at 8 slice boundaries), a map fitted to those
+        counts (mapfit), and its swaps applied between steps."""
+        nonlocal swaps
+        n_slices = 8
+        edges = [prof * (j + 1) // n_slices for j in range(n_slices)]
+
+        def snapshot():
+            moe.moe_usage_counts(counts, snap, stream=main_s)
+            main_s.synchronize()
+            return snap.numpy().copy()
+
+        prev, slices = snapshot(), []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(prof):
+            step(s, False)
+            if s + 1 in edges:
+                cur = snapshot()
+                slices.append(mapfit.counts_between(prev, cur))
+                prev = cur
+                log(f"profile: {s + 1}/{prof} steps")
+        torch.cuda.synchronize()
+        t_prof = time.perf_counter() - t0
+        total = mapfit.score(slices)
+        floor = min(mapfit.MIN_TOKENS_PER_LAYER, prof * T)
+        fitted = mapfit.fit_maps(total, n_cold, top_k=k, min_tokens=floor)
+        boot_share = float(sum(total[l, cold_owner[l]].sum() for l in range(Lr)) / total.sum())
+        changed = [mapfit.changed_cold(cold_owner[l], fitted[l].cold_owner) for l in range(Lr)]
+        before = swaps
+        t0 = time.perf_counter()
+        props = swaps_to(hot_owner, cold_owner, [m.hot_owner for m in fitted])
+        ok, bad = apply_swaps(props)
+        torch.cuda.synchronize()
+        t_apply = time.perf_counter() - t0
+        swaps = before  # the timed run's own swap count stays that of the on-line policy
+        # the swaps keep rows where they are, so compare hot sets, not row maps
+        if bad or not all(set(hot_owner[l].tolist()) == set(fitted[l].hot_owner.tolist())
+                          for l in range(Lr)):
+            raise RuntimeError("the fitted map was not applied")
+        info = {"profile_steps": prof, "profile_tokens_per_layer": prof * T,
+                "floor_tokens_per_layer": floor,
+                "profile_us_per_layer": round(t_prof * 1e6 / (prof * lps), 1),
+                "boot_cold_share_of_profile": round(boot_share, 4),
+                "fitted_cold_share_in_sample": round(mapfit.overall_cold_share(total, fitted), 4),
+                "fitted_cold_share_leave_one_slice_out": [
+                    round(x, 4) for x in mapfit.leave_one_out(slices, n_cold)],
+                "cold_ids_changed_per_layer": round(float(np.mean(changed)), 1),
+                "swaps_to_apply": ok, "apply_ms": round(t_apply * 1e3, 1),
+                "device_maps_equal_host": all(
+                    np.array_equal(maps_dev[l].cpu().numpy(), maps_host[l]) for l in range(Lr))}
+        log(f"refit {info}")
+        return info
+
     graph = None
     if args.graph:
         # one captured graph per step: every layer call reads fixed input
@@ -427,7 +500,9 @@ def main():
                 layer_call(j, False, (ids_st[j], w_st[j], x_st[j]))
 
     with torch.cuda.stream(main_s):
-        for s in range(args.warmup):
+        if refit:
+            refit_info = profile_and_refit()
+        for s in range(prof, base):
             step(s, False)
         torch.cuda.synchronize()
         if args.graph:
@@ -454,7 +529,7 @@ def main():
         map_versions = [(0, [m.copy() for m in maps_host])]
         host_us, marks, win_t, win_swaps = [], [], t0, 0
         for i in range(args.steps):
-            s = args.warmup + i
+            s = base + i
             h0 = time.perf_counter()
             step(s, True)
             host_us.append((time.perf_counter() - h0) * 1e6)
@@ -475,7 +550,7 @@ def main():
     starts = [v[0] for v in map_versions]
     cold_by_step = []
     for i in range(args.steps):
-        s = args.warmup + i
+        s = base + i
         step_bytes = step_cold = 0
         for j in range(lps):
             c = s * lps + j
@@ -492,7 +567,7 @@ def main():
         bytes_step.append(step_bytes)
         cold_by_step.append(step_cold)
     windows = [{"steps": [i - 127, i + 1],
-                **({"phase": "ABA"[phase_of((args.warmup + i) * lps)]} if shift else {}),
+                **({"phase": "ABA"[phase_of((base + i) * lps)]} if shift else {}),
                 "cold_share_of_picks": round(sum(cold_by_step[i - 127:i + 1]) / (128 * lps * T * k),
                                              4),
                 "us_per_layer": round(dt * 1e6 / (128 * lps), 1),
@@ -587,6 +662,7 @@ def main():
         "swaps_applied": swaps, "swaps_stale": stale,
         **({"windows": windows} if (off_domain or shift) else {}),
         **({"restore": restore} if restore else {}),
+        **({"refit": refit_info} if refit else {}),
         "percentiles_us": {name: pct(v) for name, v in (("step", st_ms), ("hot_gate_up", gu_ms),
                                                         ("hot_down", dn_ms), ("cold_path", c_ms))},
         # host time to enqueue one step (no waiting): it must stay below the
@@ -603,7 +679,7 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E,
-                                              b13 + b2, account, log, lps)
+                                              b13 + b2, account, log, lps, first=base)
     print(json.dumps(result), flush=True)
 
 
@@ -803,13 +879,15 @@ def cpu_baseline_prefill(args, ids, w, layer, H, I, E, gpu_ms, log):
                       "and cold, plus finalize), time scaled by 4096/48"}
 
 
-def cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E, bexp, account, log, lps=1):
+def cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E, bexp, account, log, lps=1,
+                 first=None):
     """The oracle on sampled steps of the same workload (whole layer: all picks,
     hot and cold, plus finalize), until about 10 s of CPU time."""
     import oracle
     import synth
     t_tot, b_tot, n = 0.0, 0.0, 0
-    for s in range(args.warmup, args.warmup + min(args.steps, 4)):
+    first = args.warmup if first is None else first
+    for s in range(first, first + min(args.steps, 4)):
         c = s * lps  # the step's first layer call
         l = c % Lr
         ids = ids_np[c]

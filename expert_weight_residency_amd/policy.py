@@ -93,20 +93,32 @@ class AdaptivePolicy:
         return props[: c.swaps_per_barrier]
 
 
-def restore_swaps(hot_owner: list, cold_owner: list, boot_hot_owner: list,
-                  limit: int | None = None) -> list:
-    """Swaps that return every layer to its boot-time hot set: each expert that
-    is hot now but was cold at boot is exchanged with one that is cold now but
-    was hot at boot (both in ascending expert order). At most `limit` swaps in
-    total (None: all); call again after applying them until none are left."""
+def swaps_to(hot_owner: list, cold_owner: list, target_hot: list,
+             limit: int | None = None) -> list:
+    """Swaps that turn each layer's live hot set into target_hot[l] (owners as
+    the banks hold them now): each exchanges a hot expert that the target
+    places cold with a cold expert that it places hot, both in ascending
+    expert order. At most `limit` in total (None: all); after applying them,
+    call again until none are left. Raises ValueError if a target is not a
+    hot set of that layer's experts of the bank's size."""
     props = []
-    for layer, (ho, co, bh) in enumerate(zip(hot_owner, cold_owner, boot_hot_owner)):
-        boot_hot = set(int(e) for e in bh)
-        out = sorted((int(e), r) for r, e in enumerate(ho) if int(e) not in boot_hot)
-        back = sorted((int(e), r) for r, e in enumerate(co) if int(e) in boot_hot)
+    for layer, (ho, co, th) in enumerate(zip(hot_owner, cold_owner, target_hot)):
+        want = set(int(e) for e in th)
+        out = sorted((int(e), r) for r, e in enumerate(ho) if int(e) not in want)
+        back = sorted((int(e), r) for r, e in enumerate(co) if int(e) in want)
+        if len(want) != len(ho) or len(out) != len(back):
+            raise ValueError(f"layer {layer}: target is not a hot set of {len(ho)} of this "
+                             f"layer's experts")
         for (eh, r), (ec, b) in zip(out, back):
             props.append(Swap(layer, r, b, eh, ec, 0.0))
     return props if limit is None else props[:limit]
+
+
+def restore_swaps(hot_owner: list, cold_owner: list, boot_hot_owner: list,
+                  limit: int | None = None) -> list:
+    """Swaps that return every layer to its boot-time hot set (swaps_to the
+    boot hot sets)."""
+    return swaps_to(hot_owner, cold_owner, boot_hot_owner, limit)
 
 
 class RuntimeControl:

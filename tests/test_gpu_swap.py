@@ -115,3 +115,60 @@ def test_usage_counts_snapshot():
     torch.cuda.synchronize()
     assert np.array_equal(dst.numpy(), table.cpu().numpy())
     assert dst.numel() * 4 == 61_440
+
+
+def test_refit_from_device_counts():
+    """A count-only profile on the positional boot map (~23% of picks cold),
+    counted on the device by moe_route_split, equals the host's count of the
+    same picks; the map fitted to it (mapfit) is applied with moe_swap_rows
+    and leaves the layer output bit-identical, the banks byte-equal to the
+    oracle's swaps, and far fewer picks cold."""
+    from expert_weight_residency_amd import mapfit
+    from expert_weight_residency_amd.layer import LayerBuffers
+    from expert_weight_residency_amd.policy import swaps_to
+    rm, ho, co = synth.positional_map(E, N_COLD)
+    hot_h, cold_h = host_bank(ho, SEED, 0, H, I), host_bank(co, SEED, 0, H, I)
+    hot, cold = device_bank(hot_h), pinned_bank(cold_h)
+    ob_hot = oracle.Bank(**{k: v.copy() for k, v in hot_h.items()})
+    ob_cold = oracle.Bank(**{k: v.copy() for k, v in cold_h.items()})
+    rm_dev = torch.from_numpy(rm.copy()).cuda()
+    staging = torch.empty(moe.moe_expert_bytes(H, I), dtype=torch.uint8, device="cuda")
+    counts = torch.zeros((1, E), dtype=torch.int32, device="cuda")
+    snap = torch.empty((1, E), dtype=torch.int32, pin_memory=True)
+    T, steps = 16, 40
+    bufs = LayerBuffers.allocate(T, K, H, I, len(ho), len(co))
+    host_counts = np.zeros((1, E), np.int64)
+    moe.moe_usage_counts(counts, snap)
+    torch.cuda.synchronize()
+    before = snap.numpy().copy()
+    for s in range(steps):
+        ids, _ = synth.skewed_routing(T, K, E, SEED, 0, 100 + s)
+        np.add.at(host_counts[0], ids.ravel(), 1)
+        moe.moe_route_split(torch.from_numpy(ids).cuda(), rm_dev, len(ho), len(co),
+                            bufs.hot_split, bufs.cold_split, bufs.n_invalid, counts[0], 256)
+    moe.moe_usage_counts(counts, snap)
+    torch.cuda.synchronize()
+    prof = mapfit.counts_between(before, snap.numpy())
+    assert np.array_equal(prof, host_counts)
+    fitted = mapfit.fit_maps(prof, N_COLD, top_k=K, min_tokens=T * steps)[0]
+    boot_share = host_counts[0, co].sum() / host_counts.sum()
+
+    ids, w = synth.skewed_routing(T, K, E, SEED, 0, 1)
+    x = synth.activations(T, H, SEED, step=1)
+    out0 = _layer(hot, cold, rm, ids, w, x)
+    rm_host = rm.copy()
+    props = swaps_to([ho], [co], [fitted.hot_owner])
+    assert len(props) == mapfit.changed_cold(co, fitted.cold_owner) > 0
+    for sw in props:
+        a, b, e_h, e_c = sw.hot_row, sw.cold_row, sw.expect_hot_expert, sw.expect_cold_expert
+        moe.moe_swap_rows(hot, cold, a, b, e_h, e_c, rm_dev, ho, co, staging, H, I)
+        oracle.swap_rows(ob_hot, ob_cold, a, b, e_h, e_c, rm_host, *_mirrors(ho, co, a, b, e_h, e_c))
+    torch.cuda.synchronize()
+    assert np.array_equal(rm_dev.cpu().numpy(), rm_host)
+    assert set(ho.tolist()) == set(fitted.hot_owner.tolist())
+    assert _bank_equals(hot, ob_hot) and _bank_equals(cold, ob_cold)
+    assert np.array_equal(_layer(hot, cold, rm_host, ids, w, x), out0)
+    fitted_share = host_counts[0, co].sum() / host_counts.sum()
+    print(f"refit: {len(props)} swaps, cold share {boot_share:.3f} -> {fitted_share:.3f}",
+          flush=True)
+    assert fitted_share < 0.25 * boot_share
