@@ -22,7 +22,10 @@ Prints one JSON line (see the keys below). `value` is the achieved HBM
 bandwidth of the whole step (algorithmic HBM bytes per step / wall time per
 step); `us_per_layer` is the same step time in microseconds. `roofline` covers
 the hot-bank gate/up kernel (the kernel that moves the most HBM bytes), timed
-with HIP events on its stream. `cpu_baseline` is the CPU oracle on sampled
+with HIP events on its stream. Per-kernel events are recorded on every 8th
+timed step of a long run (--event-stride): each event on a step's critical
+path adds about 5 us to that step, and the step time is the wall clock over
+all timed steps. `cpu_baseline` is the CPU oracle on sampled
 steps of the same workload.
 """
 from __future__ import annotations
@@ -50,7 +53,7 @@ NOMINAL_LINK_GBPS = 63.0
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--layers", type=int, default=8, help="distinct layer banks rotated through")
     ap.add_argument("--tokens", type=int, default=16)
@@ -90,6 +93,11 @@ def parse():
                          "per-window term, fitted to the pages' touched-set curve; auto: window "
                          "for the 7-token workloads and highconc (16 windows of 7), independent "
                          "for decode and prefill")
+    ap.add_argument("--event-stride", type=int, default=None,
+                    help="record the per-kernel timing events on every n-th timed step only "
+                         "(default: 8 for runs of 512 steps or more, else 1) "
+                         "(the step time is the wall clock over all steps either way; each "
+                         "event on a step's critical path adds ~5 us to that step)")
     ap.add_argument("--ctrl", default=None,
                     help="runtime control file (JSON) read at every policy barrier: freeze, "
                          "counting, budgets, dump_counts, restore_map")
@@ -256,6 +264,8 @@ def main():
     # --- per-call inputs, generated and uploaded before timing ---------------
     # call c = step * lps + j runs on layer bank c % Lr; its routing follows that
     # bank's ranking (or, off-domain, an independent ranking of the same shape)
+    if args.event_stride is None:
+        args.event_stride = 8 if args.steps >= 512 else 1
     # steps [0, prof): the count-only profile (refit); [prof, base): warm-up;
     # [base, S): timed
     prof = -(-args.profile_tokens // args.tokens) if refit else 0
@@ -302,6 +312,7 @@ def main():
 
     ev = {name: [] for name in ("gu0", "gu1", "dn1", "c0", "c1", "s0", "s1")}
     bytes_step, hot_bytes_gu, cold_bytes, uh_list, uc_list, cold_picks = [], [], [], [], [], 0
+    uh_first = []  # distinct hot experts of each step's first layer call (the timed one)
 
     def account(c, rm):
         ids = ids_np[c]
@@ -528,10 +539,14 @@ def main():
         # after the timed loop, on the map each call saw
         map_versions = [(0, [m.copy() for m in maps_host])]
         host_us, marks, win_t, win_swaps = [], [], t0, 0
+        sampled = []  # timed steps whose kernels carry timing events
         for i in range(args.steps):
             s = base + i
+            timed = i % max(1, args.event_stride) == 0
+            if timed:
+                sampled.append(i)
             h0 = time.perf_counter()
-            step(s, True)
+            step(s, timed)
             host_us.append((time.perf_counter() - h0) * 1e6)
             if not args.no_policy and (s + 1) % policy.cfg.read_every == 0:
                 before = swaps
@@ -560,6 +575,7 @@ def main():
             if j == 0:
                 hot_bytes_gu.append(gu)
                 cold_bytes.append(cb)
+                uh_first.append(uh)
             uh_list.append(uh)
             uc_list.append(uc)
             cold_picks += pc
@@ -602,11 +618,14 @@ def main():
                        np.array_equal(maps_dev[l].cpu().numpy(), maps_host[l]) for l in range(Lr))}
     # per-kernel events exist only for eager steps (not inside a replayed graph)
     kern = len(gu_ms) > 0
-    has_cold = np.array([b > 0 for b in cold_bytes[-len(gu_ms):]], bool) if kern else None
+    sel = np.array(sampled, np.int64)
+    hot_bytes_gu_s = np.asarray(hot_bytes_gu, np.float64)[sel]
+    cold_bytes_s = np.asarray(cold_bytes, np.float64)[sel]
+    has_cold = cold_bytes_s > 0 if kern else None
     mean_us = lambda v: round(float(v.mean() * 1e3), 1) if len(v) else None
-    achieved = float(np.sum(hot_bytes_gu) / (gu_ms.sum() / 1e3) / 1e9) if kern else None
+    achieved = float(hot_bytes_gu_s.sum() / (gu_ms.sum() / 1e3) / 1e9) if kern else None
     value = float(np.mean(bytes_step) / (ms_per_step / 1e3) / 1e9)
-    cold_link = (float(np.sum(cold_bytes) / max(c_ms.sum() / 1e3, 1e-12) / 1e9)
+    cold_link = (float(cold_bytes_s.sum() / max(c_ms.sum() / 1e3, 1e-12) / 1e9)
                  if len(c_ms) else None)
 
     # HBM traffic of the gate/up kernel from committed rocprofv3 counter runs,
@@ -640,7 +659,7 @@ def main():
                    "weights": "mxfp4", "cold_bank": COLD_BANK[args.cold_path], "map": args.map,
                    "layer_banks_rotated": Lr, "cold_stream": not args.serial,
                    "streams": "serial" if args.serial else args.streams,
-                   "graph": bool(args.graph),
+                   "graph": bool(args.graph), "event_stride": max(1, args.event_stride),
                    "policy": not args.no_policy},
         "us_per_layer": round(ms_per_step * 1e3 / lps, 1),
         "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
@@ -650,7 +669,7 @@ def main():
                                     "with_cold": mean_us(gu_ms[has_cold])} if kern else None),
         "hot_down_us": mean_us(dn_ms),
         "cold_ffn_us": mean_us(c_ms),
-        "hot_ffn_GBps": (round(float((np.sum(uh_list) * (b13 + b2)) /
+        "hot_ffn_GBps": (round(float((np.asarray(uh_first, np.float64)[sel].sum() * (b13 + b2)) /
                                      ((gu_ms.sum() + dn_ms.sum()) / 1e3) / 1e9), 1) if kern
                          else None),
         "cold_link": {"achieved_GBps": round(cold_link, 1) if cold_link is not None else None,
