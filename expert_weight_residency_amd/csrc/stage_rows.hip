@@ -23,9 +23,12 @@ constexpr uint64_t kPiece = kThreads * kUnroll;     // granules per piece (64 KB
 // The copy is cut into pieces of 64 KB (the last piece of a tensor row may be
 // shorter): per active row, ceil(row bytes / 64 KB) pieces of each tensor in
 // turn (none for a tensor passed with zero row bytes: not copied). Workgroup b takes pieces b, b + G, ...; in a piece each thread moves
-// 4 granules, consecutive lanes on consecutive granules. (Measured on the
-// host link: 8 x 1024 threads with 4 granules in flight per thread stream at
-// the link's rate; 8 in flight or 256-thread workgroups fall short.)
+// 4 granules, consecutive lanes on consecutive granules. (The compiler keeps
+// the 4 granules in LDS and issues their loads one after another, so a
+// workgroup has 16 KB in flight. Variants with all 4, or two pieces' 8, in
+// flight in registers copied at the same rate beside the hot FFN and slowed
+// the hot kernels a little more: the link, not the copy, sets the rate.
+// 256-thread workgroups fall short.)
 __global__ __launch_bounds__(kThreads) void stage_rows_kernel(
     const uint8_t* __restrict__ s0, const uint8_t* __restrict__ s1,
     const uint8_t* __restrict__ s2, const uint8_t* __restrict__ s3, uint8_t* __restrict__ d0,
