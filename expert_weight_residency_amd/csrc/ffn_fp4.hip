@@ -77,9 +77,8 @@ constexpr int kFmtFp4 = 4, kFmtFp8 = 0;  // the instruction's operand format cod
 constexpr int kLoadsPerChunk = 3 * kGroups;  // a chunk of weights: per group 2 x 16 B + scales
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wavefront are outstanding (other counters untouched).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-// ... and also until all of this wavefront's LDS reads have returned.
+// this wavefront are outstanding and all of its LDS reads have returned (the
+// export counter untouched).
 constexpr int vmcnt_lds_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
 // Workgroup barrier after an explicit wait (waitcnt immediate W), with an

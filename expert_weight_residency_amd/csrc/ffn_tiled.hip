@@ -5,7 +5,7 @@
 // Hot Experts", section "Results, September 17"), organised for calls where
 // an expert has tens of tokens ("We Built the Counter", section 7: bigger
 // steps want larger tiles than decode's 8 tokens). It runs below 256 tokens
-// per step, when a bank averages 16 or more picks per row; from 256 tokens
+// per step, when a bank averages 2 or more picks per row; from 256 tokens
 // (prefill) the FP4 kernels of ffn_fp4.hip take over.
 //
 //  - Work item = (tile of up to 64 of one expert's slots, block of 512 weight

@@ -77,8 +77,13 @@ int device_cus();
 // query fails).
 size_t device_lds_per_block();
 
-// Average picks per launchable row from which the token-tiled kernels run.
-constexpr int kTiledMinPicksPerRow = 16;
+// Average picks per launchable row from which the token-tiled kernels run
+// (steps of 17..255 tokens; the resident kernels take T <= 16 first). Measured
+// at H = 4096, I = 2880: the hot bank (295 rows) is faster on the decode
+// kernels up to 96 tokens of top-6 (1.95 picks per row) and on the tiled ones
+// at 112 (2.3); the staged cold bank (89 rows) is faster tiled from 48 tokens
+// (3.2), equal at 32 (2.2), slower at 20 (1.35).
+constexpr int kTiledMinPicksPerRow = 2;
 // Wavefronts that read a host-resident bank at once in the token-tiled kernels.
 constexpr int kTiledHostWaves = 64;
 bool ffn_use_tiled(int T, int k, int cap);

@@ -116,8 +116,8 @@ def test_decode_T7_every_slot(banks, routing):
 
 def test_decode_T112_positional_map_staged(banks):
     """High-concurrency step (112 tokens) with the positional map (the last 89
-    ids cold, ~23% of picks): the decode gate/up family (T > 16) and the
-    persistent down kernel; the cold path staged into HBM on a side stream
+    ids cold, ~23% of picks): the token-tiled kernels for both banks (2.3
+    and 7.6 picks per row); the cold path staged into HBM on a side stream
     gives the bits of the in-place cold path; sampled tokens (incl. cold
     picks) against the oracle."""
     _, ho, co, hot, cold = banks

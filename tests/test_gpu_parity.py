@@ -197,6 +197,8 @@ FFN_CASES = [
     ("many_tokens_one_expert", 32, 2, 256, 192, 100, 8, "skewed", 3),
     ("k1_T1", 16, 1, 256, 128, 1, 4, "gaussian", None),
     ("H4096_I2880_small_E", 8, 2, 4096, 2880, 6, 2, "gaussian", None),
+    # 40 picks: the hot bank (48 rows) on the decode kernels, the cold (16) tiled
+    ("decode_family_T20", 64, 2, 1024, 512, 20, 16, "skewed", None),
 ]
 
 

@@ -88,7 +88,7 @@ def test_resident_equals_decode_kernel_bitwise(where):
     """The first 4 tokens of a 20-token step (T > 16: decode kernel) and the
     same 4 tokens alone (resident kernel) give identical Y rows, with every
     expert in HBM or every expert in pinned host memory."""
-    E, k, H, I, T = 16, 2, 4096, 2880, 20
+    E, k, H, I, T = 24, 2, 4096, 2880, 20  # 40 picks on 24 rows: the decode kernels
     all_map, owners, _ = synth.all_hot_map(E)
     arrays = host_bank(owners, 13, 0, H, I)
     ids, w = synth.gaussian_routing(T, k, E, 13)

@@ -1,7 +1,7 @@
 """GPU parity of the token-tiled expert FFN (steps with many picks per row).
 
 Below 256 tokens per step the library runs the token-tiled kernels when a call
-averages at least 16 picks per launchable bank row, and the decode kernels
+averages at least 2 picks per launchable bank row, and the decode kernels
 otherwise; both are meant to give the same bits for every pick (steps of 256
 tokens and more take the FP4 path, tested in test_gpu_fp4.py). Every step
 here has fewer than 256 tokens. Checked here:
@@ -27,7 +27,7 @@ from gpu_util import (MAX_REL, REL_L2, device_bank, host_bank, oracle_bank, pinn
 
 pytestmark = pytest.mark.gpu
 
-TILED_MIN_PICKS_PER_ROW = 16  # the library's switch-over (average picks per launchable row)
+TILED_MIN_PICKS_PER_ROW = 2  # the library's switch-over (average picks per launchable row)
 
 
 @pytest.fixture(scope="module", autouse=True)
