@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=8, help="distinct layer banks rotated through")
     ap.add_argument("--tokens", type=int, default=16)
     ap.add_argument("--map", default="fitted", choices=["fitted", "positional"])
+    ap.add_argument("--cold-rows", type=int, default=89,
+                    help="rows of each layer's cold bank (the rest of the 384 experts are hot); "
+                         "89 is the workload's split, fewer show the effect of a larger HBM budget")
     ap.add_argument("--serial", action="store_true", help="cold FFN on the main stream")
     ap.add_argument("--no-policy", action="store_true", help="no counter reads or swaps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -227,7 +230,9 @@ def main():
     if routing == "auto":
         routing = "window" if args.workload in ("step40", "highconc", "offdomain",
                                                  "domainshift", "refit") else "independent"
-    n_cold = 89
+    n_cold = args.cold_rows
+    if not 0 <= n_cold <= E:
+        sys.exit(f"--cold-rows must be in [0, {E}]")
     n_hot = E - n_cold
     Lr, seed = args.layers, args.seed
     sz = synth.expert_sizes(H, I)
@@ -746,7 +751,9 @@ def run_prefill(args):
     from expert_weight_residency_amd.layer import ColdStage, LayerBuffers, enqueue_cold_ffn
 
     E, k, H, I, T = 384, 6, 4096, 2880, 4096
-    n_cold = 89
+    n_cold = args.cold_rows
+    if not 0 <= n_cold <= E:
+        sys.exit(f"--cold-rows must be in [0, {E}]")
     n_hot = E - n_cold
     Lr, seed = min(args.layers, 2), args.seed
     sz = synth.expert_sizes(H, I)
