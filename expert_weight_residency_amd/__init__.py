@@ -107,8 +107,28 @@ def _stream(stream):
     return getattr(stream, "cuda_stream", stream)
 
 
-def _ptr(t):
-    return None if t is None else t.data_ptr()
+# Host-side argument checks (a wrong dtype, a CPU tensor or a strided view
+# would otherwise reach the kernels as a raw pointer). They raise MoeError
+# with MOE_EINVAL before anything is enqueued.
+_BF16_BITS = ("torch.int16", "torch.bfloat16", "torch.uint16")
+
+
+def _bad(name: str, want: str, t) -> MoeError:
+    got = f"{getattr(t, 'dtype', type(t).__name__)} on {getattr(t, 'device', '?')}"
+    return MoeError(MOE_EINVAL, f"{name}: need {want}, got {got}")
+
+
+def _gpu(t, name: str, dtypes=None):
+    """Data pointer of a contiguous GPU tensor of one of `dtypes` (str names)."""
+    dev = getattr(t, "device", None)
+    if dev is None or dev.type != "cuda" or not t.is_contiguous() or \
+            (dtypes is not None and str(t.dtype) not in dtypes):
+        raise _bad(name, f"a contiguous GPU tensor ({', '.join(dtypes or ('any dtype',))})", t)
+    return t.data_ptr()
+
+
+def _gpu_opt(t, name: str, dtypes=None):
+    return None if t is None else _gpu(t, name, dtypes)
 
 
 def moe_expert_bytes(H: int, I: int) -> int:
@@ -141,6 +161,13 @@ class Bank:
         key = (id(self.w13), id(self.s13), id(self.w2), id(self.s2), self.on_host)
         c = self.__dict__.get("_abi")
         if c is None or c[0] != key:
+            for name, t in self.tensors().items():
+                if str(t.dtype) != "torch.uint8" or not t.is_contiguous():
+                    raise _bad(f"bank {name}", "a contiguous uint8 tensor", t)
+                if self.on_host and (t.device.type != "cpu" or not t.is_pinned()):
+                    raise _bad(f"bank {name}", "pinned host memory (on_host=True)", t)
+                if not self.on_host and t.device.type != "cuda":
+                    raise _bad(f"bank {name}", "GPU memory (on_host=False)", t)
             c = (key, MoeBankC(self.w13.data_ptr(), self.s13.data_ptr(), self.w2.data_ptr(),
                                self.s2.data_ptr(), self.n_rows, 1 if self.on_host else 0))
             self.__dict__["_abi"] = c
@@ -171,8 +198,9 @@ class Split:
         key = (id(self.n_active), id(self.active_rows), id(self.row_off), id(self.slots))
         c = self.__dict__.get("_abi")
         if c is None or c[0] != key:
-            c = (key, MoeSplitC(self.n_active.data_ptr(), self.active_rows.data_ptr(),
-                                self.row_off.data_ptr(), self.slots.data_ptr()))
+            ptrs = [_gpu(getattr(self, f), f"split {f}", ("torch.int32",))
+                    for f in ("n_active", "active_rows", "row_off", "slots")]
+            c = (key, MoeSplitC(*ptrs))
             self.__dict__["_abi"] = c
         return c[1]
 
@@ -188,32 +216,38 @@ class Split:
 def moe_route_split(topk_ids, row_map, n_hot_rows: int, n_cold_rows: int, hot: Split, cold: Split,
                     n_invalid, counts_layer=None, count_tmax: int = 256, stream=None) -> None:
     T, k = int(topk_ids.shape[0]), int(topk_ids.shape[1])
-    _check(lib().moe_route_split(_ptr(topk_ids), T, k, row_map.data_ptr(), int(row_map.shape[0]),
-                                 n_hot_rows, n_cold_rows, _ptr(counts_layer), count_tmax,
-                                 hot.abi(), cold.abi(), n_invalid.data_ptr(), _stream(stream)))
+    i32 = ("torch.int32",)
+    _check(lib().moe_route_split(_gpu(topk_ids, "topk_ids", i32), T, k,
+                                 _gpu(row_map, "row_map", i32), int(row_map.shape[0]),
+                                 n_hot_rows, n_cold_rows, _gpu_opt(counts_layer, "counts", i32),
+                                 count_tmax, hot.abi(), cold.abi(),
+                                 _gpu(n_invalid, "n_invalid", i32), _stream(stream)))
 
 
 def moe_expert_ffn_mxfp4(bank: Bank, split: Split, x, k: int, I: int, workspace, Y,
                          stream=None) -> None:
     T, H = int(x.shape[0]), int(x.shape[1])
     b = bank.abi()
-    _check(lib().moe_expert_ffn_mxfp4(ctypes.byref(b), split.abi(), x.data_ptr(), T, k, H, I,
-                                      workspace.data_ptr(), Y.data_ptr(), _stream(stream)))
+    _check(lib().moe_expert_ffn_mxfp4(ctypes.byref(b), split.abi(), _gpu(x, "x", _BF16_BITS), T, k,
+                                      H, I, _gpu(workspace, "workspace"),
+                                      _gpu(Y, "Y", _BF16_BITS), _stream(stream)))
 
 
 def moe_expert_gate_up_mxfp4(bank: Bank, split: Split, x, k: int, I: int, workspace,
                              stream=None) -> None:
     T, H = int(x.shape[0]), int(x.shape[1])
     b = bank.abi()
-    _check(lib().moe_expert_gate_up_mxfp4(ctypes.byref(b), split.abi(), x.data_ptr(), T, k, H, I,
-                                          workspace.data_ptr(), _stream(stream)))
+    _check(lib().moe_expert_gate_up_mxfp4(ctypes.byref(b), split.abi(), _gpu(x, "x", _BF16_BITS),
+                                          T, k, H, I, _gpu(workspace, "workspace"),
+                                          _stream(stream)))
 
 
 def moe_expert_down_mxfp4(bank: Bank, split: Split, T: int, k: int, H: int, I: int, workspace, Y,
                           stream=None) -> None:
     b = bank.abi()
     _check(lib().moe_expert_down_mxfp4(ctypes.byref(b), split.abi(), T, k, H, I,
-                                       workspace.data_ptr(), Y.data_ptr(), _stream(stream)))
+                                       _gpu(workspace, "workspace"), _gpu(Y, "Y", _BF16_BITS),
+                                       _stream(stream)))
 
 
 STAGE_GATE_UP, STAGE_DOWN, STAGE_ALL = 1, 2, 3
@@ -226,33 +260,44 @@ def moe_stage_rows(src: Bank, split: Split, T: int, k: int, dst: Bank, dst_rows,
     returns the split that drives the expert FFN on dst."""
     s, d = src.abi(), dst.abi()
     _check(lib().moe_stage_rows(ctypes.byref(s), split.abi(), T, k, ctypes.byref(d),
-                                dst_rows.data_ptr(), H, I, int(parts), _stream(stream)))
+                                _gpu(dst_rows, "dst_rows", ("torch.int32",)), H, I, int(parts),
+                                _stream(stream)))
     return Split(split.n_active, dst_rows, split.row_off, split.slots)
 
 
 def moe_finalize(Y, topk_w, out, stream=None) -> None:
     T, k = int(topk_w.shape[0]), int(topk_w.shape[1])
     H = int(out.shape[1])
-    _check(lib().moe_finalize(Y.data_ptr(), topk_w.data_ptr(), T, k, H, out.data_ptr(),
-                              _stream(stream)))
+    _check(lib().moe_finalize(_gpu(Y, "Y", _BF16_BITS), _gpu(topk_w, "topk_w", ("torch.float32",)),
+                              T, k, H, _gpu(out, "out", _BF16_BITS), _stream(stream)))
 
 
 def moe_usage_counts(counts, host_dst, stream=None) -> None:
     L, E = int(counts.shape[0]), int(counts.shape[1])
-    _check(lib().moe_usage_counts(counts.data_ptr(), L, E, host_dst.data_ptr(), _stream(stream)))
+    if str(getattr(host_dst, "dtype", "")) != "torch.int32" or host_dst.device.type != "cpu" or \
+            not host_dst.is_pinned() or not host_dst.is_contiguous():
+        raise _bad("host_dst", "a contiguous pinned host int32 tensor", host_dst)
+    _check(lib().moe_usage_counts(_gpu(counts, "counts", ("torch.int32",)), L, E,
+                                  host_dst.data_ptr(), _stream(stream)))
 
 
 def moe_swap_rows(hot: Bank, cold: Bank, hot_row: int, cold_row: int, expect_hot_expert: int,
                   expect_cold_expert: int, row_map, hot_owner, cold_owner, staging, H: int, I: int,
                   stream=None) -> None:
     """hot_owner / cold_owner: host int32 arrays (numpy or CPU torch), updated in place."""
-    hb, cb = hot.abi(), cold.abi()
 
     def hptr(a):
         return a.ctypes.data if hasattr(a, "ctypes") else a.data_ptr()
 
+    for name, a in (("hot_owner", hot_owner), ("cold_owner", cold_owner)):
+        if str(a.dtype) not in ("int32", "torch.int32") or \
+                not (a.flags["C_CONTIGUOUS"] if hasattr(a, "flags") else a.is_contiguous()) or \
+                getattr(getattr(a, "device", None), "type", "cpu") != "cpu":
+            raise _bad(name, "a contiguous host int32 array", a)
+    hb, cb = hot.abi(), cold.abi()
     nbytes = staging.numel() * staging.element_size()
     _check(lib().moe_swap_rows(ctypes.byref(hb), ctypes.byref(cb), hot_row, cold_row,
-                               expect_hot_expert, expect_cold_expert, row_map.data_ptr(),
+                               expect_hot_expert, expect_cold_expert,
+                               _gpu(row_map, "row_map", ("torch.int32",)),
                                int(row_map.shape[0]), hptr(hot_owner), hptr(cold_owner),
-                               staging.data_ptr(), nbytes, H, I, _stream(stream)))
+                               _gpu(staging, "staging"), nbytes, H, I, _stream(stream)))

@@ -146,3 +146,41 @@ def test_python_errors_raise(L):
         moe._check(moe.MOE_EINVAL)
     with pytest.raises(moe.MoeStale):
         moe._check(moe.MOE_ESTALE)
+
+
+def test_binding_rejects_bad_tensors(L):
+    """CPU tensors, wrong dtypes and strided views are refused on the host
+    (MoeError, MOE_EINVAL) before any pointer reaches the library."""
+    import torch
+    cpu_i32 = torch.zeros((4, 2), dtype=torch.int32)
+    split = moe.Split(*(torch.zeros(8, dtype=torch.int32) for _ in range(4)))
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_route_split(cpu_i32, torch.zeros(8, dtype=torch.int32), 6, 2, split, split,
+                            torch.zeros(1, dtype=torch.int32))
+    assert e.value.code == moe.MOE_EINVAL and "topk_ids" in str(e.value)
+    with pytest.raises(moe.MoeError) as e:
+        split.abi()
+    assert "split n_active" in str(e.value)
+    bank = moe.Bank(*(torch.zeros((2, 4), dtype=torch.uint8) for _ in range(4)), on_host=False)
+    with pytest.raises(moe.MoeError) as e:
+        bank.abi()
+    assert "GPU memory" in str(e.value)
+    host = moe.Bank(*(torch.zeros((2, 4), dtype=torch.uint8) for _ in range(4)), on_host=True)
+    with pytest.raises(moe.MoeError) as e:  # not pinned
+        host.abi()
+    assert "pinned" in str(e.value)
+    wrong = moe.Bank(*(torch.zeros((2, 4), dtype=torch.int16) for _ in range(4)))
+    with pytest.raises(moe.MoeError) as e:
+        wrong.abi()
+    assert "uint8" in str(e.value)
+    strided = torch.zeros((4, 4), dtype=torch.int32)[:, ::2]
+    with pytest.raises(moe.MoeError):
+        moe._gpu(strided, "x", ("torch.int32",))
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_usage_counts(torch.zeros((2, 8), dtype=torch.int32),
+                             torch.zeros((2, 8), dtype=torch.int32))
+    assert "host_dst" in str(e.value)
+    ho = np.zeros(3, np.int64)
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_swap_rows(bank, bank, 0, 0, 0, 0, None, ho, ho, None, 256, 128)
+    assert "hot_owner" in str(e.value)
