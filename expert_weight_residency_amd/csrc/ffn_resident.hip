@@ -4,9 +4,10 @@
 // the routed MXFP4 expert FFN per bank), organised so that a wavefront's
 // weight stream never drains:
 //
-//  - One workgroup of 16 wavefronts per CU: for a device bank on all CUs but
-//    the few a host-bank launch beside it holds; for a bank in host memory on
-//    those few (its wavefronts keep enough reads in flight to fill the link).
+//  - One workgroup of 16 wavefronts per CU for a device bank, on all CUs but
+//    the few a host-bank launch beside it holds; for a bank in host memory, 8
+//    wavefronts per workgroup on those few (still enough reads in flight to
+//    fill the link), with the registers to hold each row's whole scale line.
 //    It stages every token row of x
 //    (T <= 16 rows of H) and the split's bookkeeping (active rows, offsets,
 //    the token of every slot) into LDS once, behind one barrier. After that
@@ -82,12 +83,34 @@ __device__ __forceinline__ void scale_quad(uint2 raw, uint32_t& x, uint32_t& y) 
   y = v[1];
 }
 
-template <int P>
-__global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
+// The 8 scale bytes of chunk c0 + q of this lane's row (the layout scale_quad
+// takes), from the row's whole 128-byte scale line held across the row's four
+// lanes: lane (r, q) holds bytes 32q .. 32q+31 (chunks 4q .. 4q+3) in blk, so
+// quad Q's piece q sits in lane (r, Q), dwords 2q and 2q+1.
+__device__ __forceinline__ uint2 quad_from_line(const uint4 (&blk)[2], int r, int q, int Q) {
+  const int src = (r + 16 * Q) << 2;
+  const uint32_t w[8] = {blk[0].x, blk[0].y, blk[0].z, blk[0].w,
+                         blk[1].x, blk[1].y, blk[1].z, blk[1].w};
+  uint32_t v[8];
+#pragma unroll
+  for (int d = 0; d < 8; ++d) v[d] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)w[d]);
+  const uint32_t x = q == 0 ? v[0] : (q == 1 ? v[2] : (q == 2 ? v[4] : v[6]));
+  const uint32_t y = q == 0 ? v[1] : (q == 1 ? v[3] : (q == 2 ? v[5] : v[7]));
+  return make_uint2(x, y);
+}
+
+// kLine (banks in host memory): 8 wavefronts per workgroup with twice the
+// registers each, and each row's scale bytes read as one 128-byte line per
+// item (2 loads of 16 bytes per lane) instead of a 32-byte piece per row
+// every 4 chunks: over the host link a read of a few bytes per row costs
+// nearly what a whole line does.
+template <int P, bool kLine>
+__global__ __launch_bounds__(kLine ? 512 : kThreads, kLine ? 2 : 4) void ffn_gate_up_resident(
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
     const int32_t* __restrict__ n_active, const int32_t* __restrict__ active_rows,
     const int32_t* __restrict__ row_off, const int32_t* __restrict__ slots,
     const __bf16* __restrict__ x, int T, int k, int H, int I, uint16_t* __restrict__ h_ws) {
+  constexpr int kT = kLine ? 512 : kThreads;
   extern __shared__ __align__(16) unsigned char smem[];
   const int kpad = (H + kChunkElems - 1) / kChunkElems * kChunkElems;
   __bf16* xs = reinterpret_cast<__bf16*>(smem);
@@ -116,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
     // entries); nothing reads them. na >= 1 here (the run is not empty).
     constexpr int kB = 8;  // granules of x per thread per batch
     const int gpr = kpad / 8, ng = T * gpr;
-    for (int i0 = 0; i0 <= na || i0 < picks; i0 += kThreads) {
+    for (int i0 = 0; i0 <= na || i0 < picks; i0 += kT) {
       const int i = i0 + tid;
       const int ir = i < na ? i : na - 1, io = i <= na ? i : na, is = i < picks ? i : picks - 1;
       const int vr = active_rows[ir], vo = row_off[io], vs = slots[is];
@@ -125,13 +148,13 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
       l_slot[is] = vs;
       l_tok[is] = vs / k;
     }
-    for (int b0 = 0; b0 < ng; b0 += kB * kThreads) {
+    for (int b0 = 0; b0 < ng; b0 += kB * kT) {
       uint4 v[kB];
       int dst[kB];
       uint32_t pad = 0;  // bit u: granule u is zero padding past H
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
-        const int gi = min(b0 + u * kThreads + tid, ng - 1);
+        const int gi = min(b0 + u * kT + tid, ng - 1);
         const int n = gi / gpr, g = gi - n * gpr;
         v[u] = *reinterpret_cast<const uint4*>(x + (size_t)n * H + (g * 8 < H ? g * 8 : 0));
         pad |= (g * 8 >= H ? 1u : 0u) << u;
@@ -219,9 +242,25 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
   static_assert(P == 3, "the ring cycle must match the 4-chunk scale quad");
   AChunk ring[P + 1][kNG];
   uint2 sraw[kNG];
+  // kLine: the scale lines of the consumer's item (cur) and of the item the
+  // prefetch cursor entered last (nxt); the consumer's next quad and whether
+  // it starts a new item or pass (then cur takes nxt)
+  uint4 sb_cur[kNG][2], sb_nxt[kNG][2];
+  int s_quad = 0;
+  bool s_new = false;
+  if constexpr (kLine) {
 #pragma unroll
-  for (int g = 0; g < kNG; ++g)
-    sraw[g] = *reinterpret_cast<const uint2*>(ps[g] + 8 * (p_c + q));
+    for (int g = 0; g < kNG; ++g) {
+      sb_cur[g][0] = *reinterpret_cast<const uint4*>(ps[g] + 32 * q);
+      sb_cur[g][1] = *reinterpret_cast<const uint4*>(ps[g] + 32 * q + 16);
+      sb_nxt[g][0] = sb_cur[g][0];
+      sb_nxt[g][1] = sb_cur[g][1];
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < kNG; ++g)
+      sraw[g] = *reinterpret_cast<const uint2*>(ps[g] + 8 * (p_c + q));
+  }
 #pragma unroll
   for (int p = 0; p < P; ++p) {
 #pragma unroll
@@ -244,6 +283,17 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
       f32x4 acc[kNG] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       for (int c = 0; c < nchunk; c += P + 1) {
         uint32_t sx[kNG], sy[kNG];
+        if constexpr (kLine) {
+          if (s_new) {
+#pragma unroll
+            for (int g = 0; g < kNG; ++g) {
+              sb_cur[g][0] = sb_nxt[g][0];
+              sb_cur[g][1] = sb_nxt[g][1];
+            }
+          }
+#pragma unroll
+          for (int g = 0; g < kNG; ++g) sraw[g] = quad_from_line(sb_cur[g], r, q, s_quad);
+        }
 #pragma unroll
         for (int g = 0; g < kNG; ++g) scale_quad(sraw[g], sx[g], sy[g]);
 #pragma unroll
@@ -254,9 +304,21 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
           p_advance();
           if (u == 0) {
             // the cursor now stands at the first chunk of the next quad
+            if constexpr (kLine) {
+              s_quad = p_c >> 2;
+              s_new = p_c == 0;
+              if (p_c == 0) {  // a new item or pass: its rows' scale lines
 #pragma unroll
-            for (int g = 0; g < kNG; ++g)
-              sraw[g] = *reinterpret_cast<const uint2*>(ps[g] + 8 * (p_c + q));
+                for (int g = 0; g < kNG; ++g) {
+                  sb_nxt[g][0] = *reinterpret_cast<const uint4*>(ps[g] + 32 * q);
+                  sb_nxt[g][1] = *reinterpret_cast<const uint4*>(ps[g] + 32 * q + 16);
+                }
+              }
+            } else {
+#pragma unroll
+              for (int g = 0; g < kNG; ++g)
+                sraw[g] = *reinterpret_cast<const uint2*>(ps[g] + 8 * (p_c + q));
+            }
           }
           float sc[kNG][2];
 #pragma unroll
@@ -292,11 +354,11 @@ __global__ __launch_bounds__(kThreads, 4) void ffn_gate_up_resident(
   }
 }
 
-template <int P>
+template <int P, bool kLine>
 hipError_t launch_p(const uint8_t* w13, const uint8_t* s13, int cap, const moe_split& sp,
                     const uint16_t* x, int T, int k, int H, int I, uint16_t* h_ws,
                     hipStream_t stream, int cus) {
-  hipLaunchKernelGGL(ffn_gate_up_resident<P>, dim3(cus), dim3(kThreads),
+  hipLaunchKernelGGL((ffn_gate_up_resident<P, kLine>), dim3(cus), dim3(kLine ? 512 : kThreads),
                      resident_lds_bytes(T, k, H, cap), stream, w13, s13, sp.n_active,
                      sp.active_rows, sp.row_off, sp.slots, reinterpret_cast<const __bf16*>(x), T,
                      k, H, I, h_ws);
@@ -320,8 +382,9 @@ hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int c
   // A bank in host memory runs on kHostBankCUs workgroups (16 wavefronts,
   // 3 chunks each in flight: enough to fill the host link); a device bank on
   // the other CUs.
-  const int grid = on_host ? kHostBankCUs : (cus > 2 * kHostBankCUs ? cus - kHostBankCUs : cus);
-  return launch_p<3>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, grid);
+  if (on_host) return launch_p<3, true>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, kHostBankCUs);
+  const int grid = cus > 2 * kHostBankCUs ? cus - kHostBankCUs : cus;
+  return launch_p<3, false>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, grid);
 }
 
 }  // namespace moe
