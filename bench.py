@@ -180,8 +180,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the residency path runs on a single MI355X and this "
-              f"build has no multi-GPU path (--gpus {args.gpus}, WORLD_SIZE {world}).",
+        print("bench.py measures one GPU: the residency path runs on a single MI355X and the "
+              f"library has no multi-GPU path (--gpus {args.gpus}, WORLD_SIZE {world}).",
               file=sys.stderr)
         sys.exit(2)
 

@@ -59,7 +59,7 @@ extern "C" {
 #define MOE_EINVAL (-1)  /* bad argument: shape, alignment, NULL, limit */
 #define MOE_EHIP (-2)    /* a HIP launch or copy reported an error */
 #define MOE_ESTALE (-3)  /* swap refused: owners changed since the decision */
-#define MOE_ENOTSUP (-4) /* configuration this build does not implement */
+#define MOE_ENOTSUP (-4) /* configuration the library does not implement */
 
 #define MOE_MAX_EXPERTS 4096
 #define MOE_MAX_ROWS 4096
