@@ -159,6 +159,43 @@ def test_decode_T112_positional_map_staged(banks):
     torch.cuda.empty_cache()
 
 
+def test_decode_T112_fitted_map_verify_windows(banks):
+    """The high-concurrency workload as benchmarked: 112 tokens in 16 verify
+    windows of 7 (correlated routing: experts with tens of tokens), the
+    fitted map; the cold bank read in place and staged into HBM give the same
+    bits; sampled tokens (every token with a cold pick among them) against the
+    oracle."""
+    rm, ho, co, hot, cold = banks
+    T = 112
+    ids, w = synth.window_routing(T, K, E, SEED, 0, 13)
+    x = synth.activations(T, H, SEED, step=13)
+    load = np.bincount(ids.ravel(), minlength=E)
+    log(f"T=112 windows: {np.count_nonzero(load)} experts, max {load.max()} tokens/expert, "
+        f"{int((rm[ids] < 0).sum())} cold picks")
+    Y0, o0, ninv = run_layer(hot, cold, rm, ids, w, x, H, I)
+    assert ninv == 0
+    from expert_weight_residency_amd.layer import ColdStage, LayerBuffers, ResidencyLayer
+    from gpu_util import routing_tensors
+    ids_d, w_d, x_d = routing_tensors(ids, w, x)
+    bufs = LayerBuffers.allocate(T, K, H, I, hot.n_rows, cold.n_rows)
+    layer = ResidencyLayer(hot, cold, torch.from_numpy(rm).cuda(), H, I,
+                           stage=ColdStage(min(len(co), T * K), H, I))
+    layer.forward(x_d, ids_d, w_d, bufs, hot_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert np.array_equal(Y0, bufs.Y[: T * K].cpu().numpy().view(np.uint16))
+    assert np.array_equal(o0, bufs.out[:T].cpu().numpy().view(np.uint16))
+    t_cold = np.nonzero((rm[ids] < 0).any(axis=1))[0]
+    busiest = int(np.argmax(load))
+    t_busy = np.nonzero((ids == busiest).any(axis=1))[0]
+    tokens = np.unique(np.concatenate([t_cold[:6], t_busy[:2], [0, T - 1]]))
+    Yr, outr = _oracle_for(ids, w, x, tokens)
+    e_y = rel_errors(Y0.reshape(T, K, H)[tokens], Yr)
+    e_o = rel_errors(o0[tokens], outr)
+    log(f"  sampled {len(tokens)} tokens: Y {e_y} out {e_o}")
+    assert e_y[0] <= REL_L2 and e_y[1] <= MAX_REL
+    assert e_o[0] <= REL_L2 and e_o[1] <= MAX_REL
+
+
 def test_prefill_T4096_sampled(banks):
     """Counter skipped (T > 256), nearly every expert touched, experts with
     hundreds of tokens; sampled tokens checked against the oracle."""
