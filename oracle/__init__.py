@@ -21,8 +21,25 @@ row swap) are written here in numpy as the plain definitions:
   then a two-element row-map write), with the stale check of "We Built the
   Counter", section 2.
 
-Parity status of every function is recorded in the test-suite pins; nothing
-here is "parity unpinned".
+Every function here is pinned by a CPU test against something other than
+itself (the OCP MX value table, closed forms, a float64 library matmul on an
+independent dequantization, brute force on tiny inputs, crafted finalize
+inputs, page-printed sizes); the pin of each function is listed next to it:
+
+- e2m1, e8m0, dequant: the OCP MX value table and exponent bit patterns,
+  every (code, scale byte) pair;
+- silu: the logistic function of scipy; f32_to_bf16: torch's rounding
+  (ties, both parities, specials);
+- expert_ffn: all-ones weights (sum of x), one-hot rows (gate/up order,
+  nibble order, scale index), a float64 numpy matmul on an independent
+  dequantization;
+- finalize: k = 1 identity, an fma-sensitive input, an order-sensitive input;
+- moe_layer: split result == unsplit result, the same picks through
+  expert_ffn one by one;
+- resolve, route_split: brute force over random tiny cases;
+- usage_count: the T*k total, the 256-token gate, the int32 wrap;
+- swap_rows: five ordered swaps at 384/295/89 geometry, a mis-ordered map
+  write that diverges, stale refusal, a round trip.
 """
 from __future__ import annotations
 
@@ -71,9 +88,6 @@ def lib():
         L.oracle_moe_layer.argtypes = ([_u8p] * 4 + [ctypes.c_int] + [_u8p] * 4 + [ctypes.c_int]
                                        + [_i32p, ctypes.c_int, _i32p, _f32p] + [ctypes.c_int] * 4
                                        + [_u16p, _u16p, _u16p, ctypes.c_int])
-        L.oracle_ffn_picks.restype = None
-        L.oracle_ffn_picks.argtypes = ([_u8p] * 4 + [_i32p, _i32p] + [ctypes.c_int] * 3
-                                       + [_u16p, _u16p, ctypes.c_int])
         L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
         _lib = L
@@ -182,18 +196,6 @@ def moe_layer(hot: Bank, cold: Bank, row_map, topk_ids, topk_w, x_bf16, H: int, 
                                  np.ascontiguousarray(x_bf16, np.uint16).reshape(-1),
                                  Y.reshape(-1), out.reshape(-1), int(nthreads))
     return Y, out, bad
-
-
-def ffn_picks(bank: Bank, rows, tok, x_bf16, H: int, I: int, nthreads: int = 0) -> np.ndarray:
-    """Expert FFN for an explicit list of (bank row, token) picks -> bf16 [n, H]."""
-    rows = np.ascontiguousarray(rows, np.int32)
-    tok = np.ascontiguousarray(tok, np.int32)
-    n = rows.shape[0]
-    Y = np.empty((n, H), np.uint16)
-    lib().oracle_ffn_picks(_flat(bank.w13), _flat(bank.s13), _flat(bank.w2), _flat(bank.s2),
-                           rows, tok, n, H, I, np.ascontiguousarray(x_bf16, np.uint16).reshape(-1),
-                           Y.reshape(-1), int(nthreads))
-    return Y
 
 
 def max_threads() -> int:

@@ -249,29 +249,6 @@ int oracle_moe_layer(const uint8_t *hw13, const uint8_t *hs13, const uint8_t *hw
     return bad;
 }
 
-/* Picks listed explicitly: for each n < n_picks, compute the FFN of expert row
- * `rows[n]` of the given bank on token x[tok[n]] and write bf16 y into
- * Y[n][H]. Used to check sampled outputs at full shapes. */
-void oracle_ffn_picks(const uint8_t *w13, const uint8_t *s13, const uint8_t *w2,
-                      const uint8_t *s2, const int32_t *rows, const int32_t *tok, int n_picks,
-                      int H, int I, const uint16_t *x, uint16_t *Y, int nthreads)
-{
-    const size_t b13 = (size_t)2 * I * (H / 2), bs13 = (size_t)2 * I * (H / 32);
-    const size_t b2 = (size_t)H * (I / 2), bs2 = (size_t)H * (I / 32);
-#ifdef _OPENMP
-    if (nthreads > 0)
-        omp_set_num_threads(nthreads);
-#else
-    (void)nthreads;
-#endif
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int n = 0; n < n_picks; ++n) {
-        size_t r = (size_t)rows[n];
-        oracle_expert_ffn(w13 + r * b13, s13 + r * bs13, w2 + r * b2, s2 + r * bs2, H, I,
-                          x + (size_t)tok[n] * H, NULL, NULL, NULL, NULL, Y + (size_t)n * H);
-    }
-}
-
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -449,3 +449,32 @@ def test_page_sizes(golden_dir):
     assert round(120 * b / 2**30, 1) == g["prefetch_bank_gib"]["value"]
     # weights alone would be 16.875 MiB: the printed 17.93 includes the scales
     assert synth.expert_sizes(H, I)["w13"] + synth.expert_sizes(H, I)["w2"] == int(16.875 * 2**20)
+
+
+# ------------------------------------------------------ layer bookkeeping --
+
+def test_layer_rows_are_per_pick_ffn_and_finalize():
+    """The layer's indexing against the per-pick definition: Y[t, j] is the
+    expert FFN of the bank row the map gives for topk_ids[t, j] on token t's
+    activations, an invalid pick gives a zero row and is counted, and out is
+    the finalize of those rows (pins the slot -> token, id -> bank row and
+    bank -> tensor offsets of the layer loop)."""
+    E, k, H, I, T, seed = 12, 3, 64, 32, 5, 21
+    row_map, ho, co = synth.random_map(E, 5, seed)
+    hot, cold = _banks_for_map(E, row_map, ho, co, H, I, seed, 0)
+    ids, w = synth.gaussian_routing(T, k, E, seed)
+    ids[2, 1] = E + 3                       # out of range: invalid
+    x = synth.activations(T, H, seed)
+    Y, out, bad = oracle.moe_layer(hot, cold, row_map, ids, w, x, H, I)
+    assert bad == 1
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            if not 0 <= e < E:
+                assert not Y[t, j].any()
+                continue
+            m = int(row_map[e])
+            b, r = (hot, m) if m >= 0 else (cold, -1 - m)
+            ref = oracle.expert_ffn(b.w13[r], b.s13[r], b.w2[r], b.s2[r], x[t], H, I)["y_bf16"]
+            assert np.array_equal(Y[t, j], ref), (t, j)
+    assert np.array_equal(out, oracle.finalize(Y, w))
