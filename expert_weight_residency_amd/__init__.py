@@ -131,6 +131,40 @@ def _gpu_opt(t, name: str, dtypes=None):
     return None if t is None else _gpu(t, name, dtypes)
 
 
+def _nbytes(t) -> int:
+    return int(t.numel()) * int(t.element_size())
+
+
+def _need(t, name: str, nbytes: int) -> None:
+    """Raise MOE_EINVAL unless tensor t holds at least nbytes bytes (a
+    too-small buffer would otherwise be written past its end on the GPU)."""
+    if _nbytes(t) < nbytes:
+        raise MoeError(MOE_EINVAL, f"{name}: holds {_nbytes(t)} bytes, the call needs {nbytes}")
+
+
+def _check_bank(bank: "Bank", H: int, I: int, name: str = "bank") -> None:
+    """Every tensor of the bank holds n_rows rows of the layout for (H, I)."""
+    R = bank.n_rows
+    want = {"w13": R * 2 * I * (H // 2), "s13": R * 2 * I * (H // 32),
+            "w2": R * H * (I // 2), "s2": R * H * (I // 32)}
+    for t, n in want.items():
+        got = int(getattr(bank, t).numel())
+        if got != n:
+            raise MoeError(MOE_EINVAL, f"{name} {t}: {got} bytes, {R} rows at H={H}, I={I} "
+                                       f"need {n}")
+
+
+def _check_split(split: "Split", n_rows: int, T: int, k: int, name: str = "split") -> None:
+    """The split's buffers hold the capacity moe_route_split writes for a bank
+    of n_rows rows at T tokens, k picks each."""
+    cap = min(n_rows, T * k)
+    for f, n in (("n_active", 1), ("active_rows", cap), ("row_off", cap + 1),
+                 ("slots", T * k)):
+        if int(getattr(split, f).numel()) < n:
+            raise MoeError(MOE_EINVAL, f"{name} {f}: {int(getattr(split, f).numel())} entries, "
+                                       f"need {n} (bank rows {n_rows}, T*k {T * k})")
+
+
 def moe_expert_bytes(H: int, I: int) -> int:
     return int(lib().moe_expert_bytes(H, I))
 
@@ -158,7 +192,8 @@ class Bank:
 
     def abi(self) -> MoeBankC:
         # built once per set of tensors (the call path stays cheap on the host)
-        key = (id(self.w13), id(self.s13), id(self.w2), id(self.s2), self.on_host)
+        key = (self.w13.data_ptr(), self.s13.data_ptr(), self.w2.data_ptr(),
+               self.s2.data_ptr(), self.n_rows, self.on_host)
         c = self.__dict__.get("_abi")
         if c is None or c[0] != key:
             for name, t in self.tensors().items():
@@ -195,7 +230,8 @@ class Split:
                    torch.zeros(max(T * k, 1), dtype=torch.int32, device=device))
 
     def abi(self) -> MoeSplitC:
-        key = (id(self.n_active), id(self.active_rows), id(self.row_off), id(self.slots))
+        key = (self.n_active.data_ptr(), self.active_rows.data_ptr(), self.row_off.data_ptr(),
+               self.slots.data_ptr())
         c = self.__dict__.get("_abi")
         if c is None or c[0] != key:
             ptrs = [_gpu(getattr(self, f), f"split {f}", ("torch.int32",))
@@ -217,6 +253,12 @@ def moe_route_split(topk_ids, row_map, n_hot_rows: int, n_cold_rows: int, hot: S
                     n_invalid, counts_layer=None, count_tmax: int = 256, stream=None) -> None:
     T, k = int(topk_ids.shape[0]), int(topk_ids.shape[1])
     i32 = ("torch.int32",)
+    E = int(row_map.shape[0])
+    _check_split(hot, n_hot_rows, T, k, "hot split")
+    _check_split(cold, n_cold_rows, T, k, "cold split")
+    _need(n_invalid, "n_invalid", 4)
+    if counts_layer is not None:
+        _need(counts_layer, "counts_layer", 4 * E)
     _check(lib().moe_route_split(_gpu(topk_ids, "topk_ids", i32), T, k,
                                  _gpu(row_map, "row_map", i32), int(row_map.shape[0]),
                                  n_hot_rows, n_cold_rows, _gpu_opt(counts_layer, "counts", i32),
@@ -224,9 +266,28 @@ def moe_route_split(topk_ids, row_map, n_hot_rows: int, n_cold_rows: int, hot: S
                                  _gpu(n_invalid, "n_invalid", i32), _stream(stream)))
 
 
+def _ffn_sizes(bank: Bank, split: Split, T: int, k: int, H: int, I: int, workspace, Y) -> None:
+    if T <= 0 or bank.n_rows == 0:
+        return
+    _check_bank(bank, H, I)
+    # The split is read here, written by moe_route_split (whose wrapper checks
+    # its capacities): a staged split pairs one bank's row lists with another
+    # bank, so only the slot list's length is fixed by this call.
+    if int(split.slots.numel()) < T * k:
+        raise MoeError(MOE_EINVAL, f"split slots: {int(split.slots.numel())} entries, "
+                                   f"need T*k = {T * k}")
+    ws = moe_ffn_workspace_bytes(T, k, H, I)
+    if ws == 0:
+        raise MoeError(MOE_ENOTSUP, f"no workspace size for T={T}, k={k}, H={H}, I={I}")
+    _need(workspace, "workspace", ws)
+    if Y is not None:
+        _need(Y, "Y", 2 * T * k * H)
+
+
 def moe_expert_ffn_mxfp4(bank: Bank, split: Split, x, k: int, I: int, workspace, Y,
                          stream=None) -> None:
     T, H = int(x.shape[0]), int(x.shape[1])
+    _ffn_sizes(bank, split, T, k, H, I, workspace, Y)
     b = bank.abi()
     _check(lib().moe_expert_ffn_mxfp4(ctypes.byref(b), split.abi(), _gpu(x, "x", _BF16_BITS), T, k,
                                       H, I, _gpu(workspace, "workspace"),
@@ -236,6 +297,7 @@ def moe_expert_ffn_mxfp4(bank: Bank, split: Split, x, k: int, I: int, workspace,
 def moe_expert_gate_up_mxfp4(bank: Bank, split: Split, x, k: int, I: int, workspace,
                              stream=None) -> None:
     T, H = int(x.shape[0]), int(x.shape[1])
+    _ffn_sizes(bank, split, T, k, H, I, workspace, None)
     b = bank.abi()
     _check(lib().moe_expert_gate_up_mxfp4(ctypes.byref(b), split.abi(), _gpu(x, "x", _BF16_BITS),
                                           T, k, H, I, _gpu(workspace, "workspace"),
@@ -244,6 +306,7 @@ def moe_expert_gate_up_mxfp4(bank: Bank, split: Split, x, k: int, I: int, worksp
 
 def moe_expert_down_mxfp4(bank: Bank, split: Split, T: int, k: int, H: int, I: int, workspace, Y,
                           stream=None) -> None:
+    _ffn_sizes(bank, split, T, k, H, I, workspace, Y)
     b = bank.abi()
     _check(lib().moe_expert_down_mxfp4(ctypes.byref(b), split.abi(), T, k, H, I,
                                        _gpu(workspace, "workspace"), _gpu(Y, "Y", _BF16_BITS),
@@ -258,6 +321,12 @@ def moe_stage_rows(src: Bank, split: Split, T: int, k: int, dst: Bank, dst_rows,
     """Copy src's active rows (per split) of the tensors `parts` names
     (STAGE_GATE_UP, STAGE_DOWN, STAGE_ALL) to rows 0.. of the device bank dst;
     returns the split that drives the expert FFN on dst."""
+    if T > 0 and src.n_rows > 0:
+        cap = min(src.n_rows, T * k)
+        _check_bank(src, H, I, "src")
+        _check_bank(dst, H, I, "dst")
+        _check_split(split, src.n_rows, T, k)
+        _need(dst_rows, "dst_rows", 4 * cap)
     s, d = src.abi(), dst.abi()
     _check(lib().moe_stage_rows(ctypes.byref(s), split.abi(), T, k, ctypes.byref(d),
                                 _gpu(dst_rows, "dst_rows", ("torch.int32",)), H, I, int(parts),
@@ -268,6 +337,9 @@ def moe_stage_rows(src: Bank, split: Split, T: int, k: int, dst: Bank, dst_rows,
 def moe_finalize(Y, topk_w, out, stream=None) -> None:
     T, k = int(topk_w.shape[0]), int(topk_w.shape[1])
     H = int(out.shape[1])
+    _need(Y, "Y", 2 * T * k * H)
+    _need(out, "out", 2 * T * H)
+    _need(topk_w, "topk_w", 4 * T * k)
     _check(lib().moe_finalize(_gpu(Y, "Y", _BF16_BITS), _gpu(topk_w, "topk_w", ("torch.float32",)),
                               T, k, H, _gpu(out, "out", _BF16_BITS), _stream(stream)))
 
@@ -277,6 +349,7 @@ def moe_usage_counts(counts, host_dst, stream=None) -> None:
     if str(getattr(host_dst, "dtype", "")) != "torch.int32" or host_dst.device.type != "cpu" or \
             not host_dst.is_pinned() or not host_dst.is_contiguous():
         raise _bad("host_dst", "a contiguous pinned host int32 tensor", host_dst)
+    _need(host_dst, "host_dst", 4 * L * E)
     _check(lib().moe_usage_counts(_gpu(counts, "counts", ("torch.int32",)), L, E,
                                   host_dst.data_ptr(), _stream(stream)))
 
@@ -294,6 +367,12 @@ def moe_swap_rows(hot: Bank, cold: Bank, hot_row: int, cold_row: int, expect_hot
                 not (a.flags["C_CONTIGUOUS"] if hasattr(a, "flags") else a.is_contiguous()) or \
                 getattr(getattr(a, "device", None), "type", "cpu") != "cpu":
             raise _bad(name, "a contiguous host int32 array", a)
+    _check_bank(hot, H, I, "hot bank")
+    _check_bank(cold, H, I, "cold bank")
+    for name, a, b in (("hot_owner", hot_owner, hot), ("cold_owner", cold_owner, cold)):
+        n = a.size if hasattr(a, "size") and not callable(a.size) else a.numel()
+        if int(n) != b.n_rows:
+            raise MoeError(MOE_EINVAL, f"{name}: {int(n)} entries for a bank of {b.n_rows} rows")
     hb, cb = hot.abi(), cold.abi()
     nbytes = staging.numel() * staging.element_size()
     _check(lib().moe_swap_rows(ctypes.byref(hb), ctypes.byref(cb), hot_row, cold_row,

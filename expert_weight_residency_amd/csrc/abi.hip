@@ -34,6 +34,11 @@ int check_dims(int T, int k, int H, int I) {
   if (I <= 0 || I % 64) return fail(MOE_EINVAL, "I=%d must be a positive multiple of 64", I);
   if (H > moe::ffn_max_reduction() || I > moe::ffn_max_reduction())
     return fail(MOE_ENOTSUP, "H=%d, I=%d: at most %d supported", H, I, moe::ffn_max_reduction());
+  if (moe::ffn_use_fp4(T) && !moe::ffn_fp4_fits(T, k, H, I))
+    return fail(MOE_ENOTSUP,
+                "T*k=%lld slots at H=%d, I=%d: the FP4 path addresses each activation region "
+                "with 32-bit offsets; split the step into smaller chunks",
+                (long long)T * k, H, I);
   return MOE_OK;
 }
 
@@ -79,7 +84,8 @@ size_t moe_expert_bytes(int H, int I) {
 
 size_t moe_ffn_workspace_bytes(int T, int k, int H, int I) {
   if (T <= 0 || k <= 0 || H <= 0 || I <= 0) return 0;
-  if (moe::ffn_use_fp4(T)) return moe::ffn_fp4_workspace_bytes(T, k, H, I);
+  if (moe::ffn_use_fp4(T))
+    return moe::ffn_fp4_fits(T, k, H, I) ? moe::ffn_fp4_workspace_bytes(T, k, H, I) : 0;
   return (size_t)T * k * I * sizeof(uint16_t);
 }
 

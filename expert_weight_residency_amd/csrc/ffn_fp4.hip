@@ -368,7 +368,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void ffn_fp4(
     // exactly one chunk of weight loads: rows past the tile's last slot copy
     // its first slot (their token columns compute values that are never
     // written out: the MFMA's output columns are independent), and the chunk
-    // index is clamped. (Byte offsets stay below 4 GB: the rows of T*k slots.)
+    // index is clamped. Source offsets are 32-bit (a 64-bit copy of each
+    // costs registers this kernel does not have): the entry points refuse
+    // steps whose quantized rows reach 4 GB (ffn_fp4_fits).
     constexpr int kU = kTok * 32 / kThreads;  // copies per wavefront per chunk
     uint32_t src_row[kU];
 #pragma unroll
@@ -579,6 +581,12 @@ Fp4Ws fp4_ws(void* ws, int T, int k, int H, int I) {
 }  // namespace
 
 bool ffn_use_fp4(int T) { return T >= kFp4MinTokens; }
+
+bool ffn_fp4_fits(int T, int k, int H, int I) {
+  const uint64_t P = (uint64_t)T * k;
+  const uint64_t nI = (I + kChunkElems - 1) / kChunkElems, nH = (H + kChunkElems - 1) / kChunkElems;
+  return P * (nI > nH ? nI : nH) * kQData < ((uint64_t)1 << 32);
+}
 
 size_t ffn_fp4_workspace_bytes(int T, int k, int H, int I) {
   const size_t P = (size_t)T * k;

@@ -95,6 +95,10 @@ bool ffn_use_tiled(int T, int k, int cap);
 // (ffn_fp4_workspace_bytes).
 constexpr int kFp4MinTokens = MOE_FP4_MIN_TOKENS;
 bool ffn_use_fp4(int T);
+// The FP4 kernels address each quantized activation region (x or h: T*k slot
+// rows of ceil(K/256) chunks of 512 data bytes) with 32-bit byte offsets;
+// false when a region would reach 4 GB (T*k >= 524,288 slots at H = 4096).
+bool ffn_fp4_fits(int T, int k, int H, int I);
 size_t ffn_fp4_workspace_bytes(int T, int k, int H, int I);
 hipError_t launch_gate_up_fp4(const uint8_t* w13, const uint8_t* s13, int cap, int on_host,
                               const moe_split& split, const uint16_t* x, int T, int k, int H,

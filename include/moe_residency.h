@@ -42,7 +42,9 @@
  *
  * Shape limits: 1 <= E <= MOE_MAX_EXPERTS; bank rows <= MOE_MAX_ROWS; H and I
  * positive multiples of 64, at most 32768; 1 <= k <= MOE_MAX_TOPK; T >= 0 and
- * T*k < 2^31.
+ * T*k < 2^31. Steps of MOE_FP4_MIN_TOKENS tokens or more also need
+ * T*k * ceil(max(H, I)/256) * 512 < 2^32 (T*k < 524,288 at H = 4096); larger
+ * ones are refused with MOE_ENOTSUP (split them into chunks).
  * Pointers to weights, activations and Y rows must be 16-byte aligned.
  */
 #ifndef MOE_RESIDENCY_H
@@ -104,7 +106,8 @@ size_t moe_expert_bytes(int H, int I);
  * MOE_FP4_MIN_TOKENS on, x and h per slot as the two E4M3 terms the FP4 path
  * reads ((T*k) * (ceil(H/256) + ceil(I/256)) * 528 bytes). Both bank calls of
  * one layer may share one workspace: each writes only its own slots. 0 when
- * any argument is <= 0. */
+ * any argument is <= 0, and for a step the FFN refuses with MOE_ENOTSUP (see
+ * the shape limits above). */
 size_t moe_ffn_workspace_bytes(int T, int k, int H, int I);
 
 /*
@@ -151,8 +154,11 @@ int moe_route_split(const int32_t *topk_ids, int T, int k, const int32_t *row_ma
  * The per-(row, slot) arithmetic, including its reduction order, does not
  * depend on the bank, the row index, the other slots or the grid, so a pick
  * gives the same bits from either bank. It depends on the step size only:
- * below MOE_FP4_MIN_TOKENS tokens the weights are dequantized to bf16 (exact)
- * for bf16 matrix products; from MOE_FP4_MIN_TOKENS on (prefill) the E2M1
+ * below MOE_FP4_MIN_TOKENS tokens the weights are dequantized to bf16 for bf16
+ * matrix products (every E2M1 value times an E8M0 scale of byte 0 .. 252 is a
+ * bf16 value, subnormals included, so the dequantization is exact there; those
+ * bytes are tested against the CPU oracle); from MOE_FP4_MIN_TOKENS on
+ * (prefill) the E2M1
  * weights and their scales go to the block-scaled FP4 matrix instruction as
  * stored, with each bf16 activation (x, and h after its bf16 rounding) carried
  * as two E4M3 terms with E8M0 per-32 scales, which hold it to within 2^-9 of
@@ -161,8 +167,11 @@ int moe_route_split(const int32_t *topk_ids, int T, int k, const int32_t *row_ma
  *
  * bank: see moe_bank. split: this bank's moe_route_split output (device).
  * x: device bf16 [T][H]. workspace: device, moe_ffn_workspace_bytes(T,k,H,I)
- * bytes. Y: device bf16 [T*k][H]. Launches two kernels (gate/up + SwiGLU,
- * then down); launches nothing when T == 0 or the bank has no rows.
+ * bytes. Y: device bf16 [T*k][H]. Below MOE_FP4_MIN_TOKENS tokens launches two
+ * kernels (gate/up + SwiGLU, then down); from MOE_FP4_MIN_TOKENS on, three
+ * (the activations' two-term split, gate/up + SwiGLU, down). Launches nothing
+ * when T == 0 or the bank has no rows. MOE_ENOTSUP for a prefill step past the
+ * FP4 path's offset limit (see the shape limits above).
  */
 int moe_expert_ffn_mxfp4(const moe_bank *bank, moe_split split, const uint16_t *x, int T, int k,
                          int H, int I, void *workspace, uint16_t *Y, void *stream);

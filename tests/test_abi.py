@@ -184,3 +184,92 @@ def test_binding_rejects_bad_tensors(L):
     with pytest.raises(moe.MoeError) as e:
         moe.moe_swap_rows(bank, bank, 0, 0, 0, 0, None, ho, ho, None, 256, 128)
     assert "hot_owner" in str(e.value)
+
+
+def test_fp4_step_past_32bit_offsets_is_refused(L):
+    """The FP4 path addresses each quantized activation region with 32-bit
+    byte offsets: a step whose region would reach 4 GB is refused before any
+    work (MOE_ENOTSUP), and its workspace size reads 0."""
+    p = 0x1000
+    bank = moe.MoeBankC(p, p, p, p, 295, 0)
+    # H = 4096: 16 chunks of 512 bytes per slot row -> 2^32 bytes at 524,288 slots
+    T_ok, T_bad = 524_287 // 6, 524_288 // 6 + 1
+    assert moe.moe_ffn_workspace_bytes(T_ok, 6, 4096, 2880) > 0
+    assert moe.moe_ffn_workspace_bytes(T_bad, 6, 4096, 2880) == 0
+    for fn in ("moe_expert_ffn_mxfp4",):
+        rc = getattr(L, fn)(ctypes.byref(bank), _split(), p, T_bad, 6, 4096, 2880, p, p, None)
+        assert rc == moe.MOE_ENOTSUP, rc
+        assert "32-bit" in moe.moe_last_error()
+    assert L.moe_expert_gate_up_mxfp4(ctypes.byref(bank), _split(), p, T_bad, 6, 4096, 2880, p,
+                                      None) == moe.MOE_ENOTSUP
+    assert L.moe_expert_down_mxfp4(ctypes.byref(bank), _split(), T_bad, 6, 4096, 2880, p, p,
+                                   None) == moe.MOE_ENOTSUP
+    # the largest hidden size: 128 chunks per row -> the limit is 65,536 slots
+    assert moe.moe_ffn_workspace_bytes(65_535 // 2, 2, 32768, 2880) > 0
+    assert moe.moe_ffn_workspace_bytes(65_536 // 2, 2, 32768, 2880) == 0
+
+
+def test_binding_rejects_undersized_buffers(L):
+    """Buffers too small for the call's sizes are refused on the host
+    (MOE_EINVAL) before anything reaches the library: workspace, Y, split
+    capacities, bank tensors that do not hold n_rows rows at (H, I), the
+    finalize's and the counter snapshot's buffers, owner mirrors."""
+    import torch
+    T, k, H, I, R = 16, 6, 256, 128, 10
+    u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)
+    bank = moe.Bank(u8(R, 2 * I, H // 2), u8(R, 2 * I, H // 32), u8(R, H, I // 2),
+                    u8(R, H, I // 32))
+    split = moe.Split.empty(R, T, k, device="cpu")
+    x = torch.zeros((T, H), dtype=torch.int16)
+    Y = torch.zeros((T * k, H), dtype=torch.int16)
+    ws = u8(moe.moe_ffn_workspace_bytes(T, k, H, I))
+
+    def raises(fn, *a, match):
+        with pytest.raises(moe.MoeError) as e:
+            fn(*a)
+        assert e.value.code == moe.MOE_EINVAL and match in str(e.value), str(e.value)
+
+    raises(moe.moe_expert_ffn_mxfp4, bank, split, x, k, I, ws[:-16], Y, match="workspace")
+    raises(moe.moe_expert_ffn_mxfp4, bank, split, x, k, I, ws, Y[:-1], match="Y")
+    raises(moe.moe_expert_down_mxfp4, bank, split, T, k, H, I, ws, Y[:-1], match="Y")
+    raises(moe.moe_expert_gate_up_mxfp4, bank, split, x, k, I, ws[:-16], match="workspace")
+    short = moe.Split(split.n_active, split.active_rows, split.row_off, split.slots[:-1])
+    raises(moe.moe_expert_ffn_mxfp4, bank, short, x, k, I, ws, Y, match="slots")
+    thin = moe.Bank(bank.w13, bank.s13, bank.w2[:, :, :-16].contiguous(), bank.s2)
+    raises(moe.moe_expert_ffn_mxfp4, thin, split, x, k, I, ws, Y, match="w2")
+    # a prefill-sized step needs the FP4 workspace, ~10x the decode one per slot
+    Tp = 256
+    raises(moe.moe_expert_ffn_mxfp4, bank, moe.Split.empty(R, Tp, k, device="cpu"),
+           torch.zeros((Tp, H), dtype=torch.int16), k, I,
+           u8(moe.moe_ffn_workspace_bytes(Tp - 1, k, H, I)),
+           torch.zeros((Tp * k, H), dtype=torch.int16), match="workspace")
+    # route split: capacities for min(rows, T*k) active rows and T*k slots
+    ids, rm, ninv = i32(T, k), i32(384), i32(1)
+    small = moe.Split(i32(1), i32(R - 1), i32(R + 1), i32(T * k))
+    raises(moe.moe_route_split, ids, rm, R, 0, small, split, ninv, match="active_rows")
+    small = moe.Split(i32(1), i32(R), i32(R), i32(T * k))
+    raises(moe.moe_route_split, ids, rm, R, 0, small, split, ninv, match="row_off")
+    small = moe.Split(i32(1), i32(R), i32(R + 1), i32(T * k - 1))
+    raises(moe.moe_route_split, ids, rm, R, 0, small, split, ninv, match="slots")
+    raises(moe.moe_route_split, ids, rm, R, 0, split, split, ninv, i32(383), match="counts")
+    # finalize and the snapshot
+    w = torch.zeros((T, k), dtype=torch.float32)
+    raises(moe.moe_finalize, Y[:-1], w, torch.zeros((T, H), dtype=torch.int16), match="Y")
+    raises(moe.moe_finalize, Y, w, torch.zeros((T - 1, H), dtype=torch.int16), match="out")
+    # owners must have one entry per bank row
+    raises(moe.moe_swap_rows, bank, bank, 0, 0, 1, 2, i32(384), np.zeros(R - 1, np.int32),
+           np.zeros(R, np.int32), u8(16), H, I, match="hot_owner")
+
+
+def test_abi_cache_follows_tensor_storage(L):
+    """The cached C struct of a bank or split is rebuilt when a field is
+    replaced by another tensor (the cache is keyed on data pointers)."""
+    import torch
+    b = moe.Bank(*(torch.zeros((2, 4), dtype=torch.uint8) for _ in range(4)))
+    key = lambda: (b.w13.data_ptr(), b.s13.data_ptr(), b.w2.data_ptr(), b.s2.data_ptr())
+    b.__dict__["_abi"] = ((key() + (b.n_rows, b.on_host)), "cached")
+    assert b.abi() == "cached"
+    b.w2 = torch.ones((2, 4), dtype=torch.uint8)   # new storage: the cache must not be used
+    with pytest.raises(moe.MoeError):               # rebuilt: CPU tensors are refused
+        b.abi()
