@@ -21,11 +21,18 @@ resident (device / pinned) before the timed region.
 Prints one JSON line (see the keys below). `value` is the achieved HBM
 bandwidth of the whole step (algorithmic HBM bytes per step / wall time per
 step); `us_per_layer` is the same step time in microseconds. `roofline` covers
-the hot-bank gate/up kernel (the kernel that moves the most HBM bytes), timed
-with HIP events on its stream. Per-kernel events are recorded on every 8th
-timed step of a long run (--event-stride): each event on a step's critical
-path adds about 5 us to that step, and the step time is the wall clock over
-all timed steps. `cpu_baseline` is the CPU oracle on sampled
+the hot-bank gate/up kernel (the kernel that moves the most HBM bytes) and
+`roofline_hot_bank` the hot bank's two GEMM kernels together, both timed with
+HIP events on the hot bank's stream in every timed step (that stream is off
+the step's critical path whenever the step has a cold pick). Events on the
+main stream (step and cold-path times) would each add ~5 us to the step, so
+they are taken in a separate untimed pass over the first timed steps
+(--profile-steps); the step time itself is the wall clock over all timed
+steps. The timed steps' routing is drawn so that their cold-expert counts
+follow the generator's distribution (quantiles of a larger draw per layer
+bank, --no-stratify to draw every step on its own): one cold expert costs
+~0.35 ms over the host link, so a short run's mean otherwise swings with how
+many the draw happens to hit. `cpu_baseline` is the CPU oracle on sampled
 steps of the same workload.
 """
 from __future__ import annotations
@@ -96,11 +103,13 @@ def parse():
                          "per-window term, fitted to the pages' touched-set curve; auto: window "
                          "for the 7-token workloads and highconc (16 windows of 7), independent "
                          "for decode and prefill")
-    ap.add_argument("--event-stride", type=int, default=None,
-                    help="record the per-kernel timing events on every n-th timed step only "
-                         "(default: 8 for runs of 512 steps or more, else 1) "
-                         "(the step time is the wall clock over all steps either way; each "
-                         "event on a step's critical path adds ~5 us to that step)")
+    ap.add_argument("--profile-steps", type=int, default=64,
+                    help="untimed pass after the timed steps, over the first n of them again, "
+                         "with events on every kernel (step, cold path and hot kernels): the "
+                         "percentiles and the cold-link rate come from it (0: none)")
+    ap.add_argument("--no-stratify", action="store_true",
+                    help="draw each timed step's routing on its own instead of at quantiles of "
+                         "cold-expert count per layer bank")
     ap.add_argument("--ctrl", default=None,
                     help="runtime control file (JSON) read at every policy barrier: freeze, "
                          "counting, budgets, dump_counts, restore_map")
@@ -269,8 +278,6 @@ def main():
     # --- per-call inputs, generated and uploaded before timing ---------------
     # call c = step * lps + j runs on layer bank c % Lr; its routing follows that
     # bank's ranking (or, off-domain, an independent ranking of the same shape)
-    if args.event_stride is None:
-        args.event_stride = 8 if args.steps >= 512 else 1
     # steps [0, prof): the count-only profile (refit); [prof, base): warm-up;
     # [base, S): timed
     prof = -(-args.profile_tokens // args.tokens) if refit else 0
@@ -290,12 +297,44 @@ def main():
     w_np = np.empty((C, T, k), np.float32)
     NX = min(C, 64)
     x_np = np.empty((NX, T, H), np.uint16)
-    for c in range(C):
-        pm = perms_b[c % Lr] if shift and phase_of(c) == 1 else perms[c % Lr]
+    def draw(l, c, pm):
         if routing == "window":
-            ids_np[c], w_np[c] = synth.window_routing(T, k, E, seed, c % Lr, c, perm=pm)
-        else:
-            ids_np[c], w_np[c] = synth.skewed_routing(T, k, E, seed, c % Lr, c, perm=pm)
+            return synth.window_routing(T, k, E, seed, l, c, perm=pm)
+        return synth.skewed_routing(T, k, E, seed, l, c, perm=pm)
+
+    # in-domain workloads on a fixed map: the timed calls of each layer bank
+    # take their routing at evenly spaced quantiles (by distinct cold experts,
+    # then distinct hot experts under the bank's boot map) of a draw four times
+    # as large, in a seeded random order
+    stratify = (not args.no_stratify and not (off_domain or shift or refit)
+                and args.workload in ("decode", "highconc", "step40"))
+    strat_info = None
+    for c in range(C if not stratify else base * lps):
+        pm = perms_b[c % Lr] if shift and phase_of(c) == 1 else perms[c % Lr]
+        ids_np[c], w_np[c] = draw(c % Lr, c, pm)
+    if stratify:
+        rng_sel = np.random.default_rng([seed, 0x57A7])
+        pool_cold, want = [], 0.0
+        for l in range(Lr):
+            calls = list(range(base * lps + ((l - base * lps) % Lr), C, Lr))
+            if not calls:
+                continue
+            P = max(4 * len(calls), 64)
+            pool = [draw(l, 1_000_000 + j, perms[l]) for j in range(P)]
+            m = maps_host[l]
+            key = []
+            for j, (ids_j, _) in enumerate(pool):
+                mm = m[ids_j]
+                key.append((len(np.unique(ids_j[mm < 0])), len(np.unique(ids_j[mm >= 0])), j))
+            key.sort()
+            pool_cold.extend(kk[0] for kk in key)
+            pick = [key[int((i + 0.5) * P / len(calls))][2] for i in range(len(calls))]
+            rng_sel.shuffle(pick)
+            for c, j in zip(calls, pick):
+                ids_np[c], w_np[c] = pool[j]
+        strat_info = {"method": "quantiles of distinct cold, then hot, experts in a 4x draw "
+                                "per layer bank",
+                      "expected_cold_experts_per_call": round(float(np.mean(pool_cold)), 3)}
     for c in range(NX):
         x_np[c] = synth.activations(T, H, seed, c % Lr, c)
     ids_d = torch.from_numpy(ids_np).cuda()
@@ -315,7 +354,9 @@ def main():
     boot_hot = [h.copy() for h in hot_owner]
     swaps = stale = 0
 
-    ev = {name: [] for name in ("gu0", "gu1", "dn1", "c0", "c1", "s0", "s1")}
+    # hot-stream events of the timed steps, and every event of the profile pass
+    ev = {name: [] for name in ("gu0", "gu1", "dn1")}
+    pev = {name: [] for name in ("gu0", "gu1", "dn1", "c0", "c1", "s0", "s1")}
     bytes_step, hot_bytes_gu, cold_bytes, uh_list, uc_list, cold_picks = [], [], [], [], [], 0
     uh_first = []  # distinct hot experts of each step's first layer call (the timed one)
 
@@ -335,12 +376,16 @@ def main():
     # Everything the timed loop records or waits on is created beforehand, so
     # the host work per step is the library calls themselves (the step must
     # stay bound by the device, not by the host enqueueing it).
-    ev_pool = [torch.cuda.Event(enable_timing=True) for _ in range(7 * (args.steps + 4))]
+    n_prof = 0 if args.graph else max(0, min(args.profile_steps, args.steps))
+    ev_pool = [torch.cuda.Event(enable_timing=True)
+               for _ in range(3 * args.steps + 7 * n_prof + 8)]
 
     def mark(name, stream):
         e = ev_pool.pop()
         e.record(stream)
-        ev[name].append(e)
+        (pev if in_profile else ev)[name].append(e)
+
+    in_profile = False  # set during the untimed profile pass
 
     fork_ev, join_hot_ev, join_cold_ev = torch.cuda.Event(), torch.cuda.Event(), torch.cuda.Event()
 
@@ -349,19 +394,21 @@ def main():
         dst.wait_event(e)
 
     def cold_ffn(xc, l, timed):
-        if timed:
+        full = timed and in_profile  # main-stream events only in the profile pass
+        if full:
             mark("c0", cold_s)
         enqueue_cold_ffn(cold[l], bufs.cold_split, xc, k, H, I, bufs, stage, cold_s,
                          overlap=not args.serial)
-        if timed:
+        if full:
             mark("c1", cold_s)
 
     def step(s, timed):
-        if timed:
+        full = timed and in_profile
+        if full:
             mark("s0", main_s)
         for j in range(lps):
             layer_call(s * lps + j, timed and j == 0)
-        if timed:
+        if full:
             mark("s1", main_s)
 
     def layer_call(c, timed, src=None):
@@ -530,28 +577,16 @@ def main():
 
             def step(s, timed):  # noqa: F811 (the graph replaces the eager step)
                 load_step(s)
-                if timed:
-                    e = torch.cuda.Event(enable_timing=True)
-                    e.record(main_s)
-                    ev["s0"].append(e)
                 graph.replay()
-                if timed:
-                    e = torch.cuda.Event(enable_timing=True)
-                    e.record(main_s)
-                    ev["s1"].append(e)
         t0 = time.perf_counter()
         # the maps in force from each layer call on: the byte accounting runs
         # after the timed loop, on the map each call saw
         map_versions = [(0, [m.copy() for m in maps_host])]
         host_us, marks, win_t, win_swaps = [], [], t0, 0
-        sampled = []  # timed steps whose kernels carry timing events
         for i in range(args.steps):
             s = base + i
-            timed = i % max(1, args.event_stride) == 0
-            if timed:
-                sampled.append(i)
             h0 = time.perf_counter()
-            step(s, timed)
+            step(s, True)
             host_us.append((time.perf_counter() - h0) * 1e6)
             if not args.no_policy and (s + 1) % policy.cfg.read_every == 0:
                 before = swaps
@@ -566,6 +601,14 @@ def main():
                 win_t, win_swaps = now, 0
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        # untimed profile pass: the first n_prof timed steps again, with events
+        # on the main stream too (step boundaries, the cold path)
+        in_profile = True
+        for i in range(n_prof):
+            step(base + i, True)
+        torch.cuda.synchronize()
+        in_profile = False
+        prof_maps = [m.copy() for m in maps_host]
 
     starts = [v[0] for v in map_versions]
     cold_by_step = []
@@ -596,10 +639,10 @@ def main():
 
     K = args.steps
     ms_per_step = (t1 - t0) * 1e3 / K
-    gu_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["gu0"], ev["gu1"])])
-    dn_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["gu1"], ev["dn1"])])
-    c_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["c0"], ev["c1"])])
-    st_ms = np.array([a.elapsed_time(b) for a, b in zip(ev["s0"], ev["s1"])])
+    ms = lambda e, a, b: np.array([x.elapsed_time(y) for x, y in zip(e[a], e[b])])
+    gu_ms, dn_ms = ms(ev, "gu0", "gu1"), ms(ev, "gu1", "dn1")       # every timed step
+    pgu_ms, pdn_ms = ms(pev, "gu0", "gu1"), ms(pev, "gu1", "dn1")   # profile pass
+    c_ms, st_ms = ms(pev, "c0", "c1"), ms(pev, "s0", "s1")
 
     def pct(v):  # p10 / median / p90 in microseconds
         return ({k: round(float(np.percentile(v, q) * 1e3), 1)
@@ -623,15 +666,21 @@ def main():
                        np.array_equal(maps_dev[l].cpu().numpy(), maps_host[l]) for l in range(Lr))}
     # per-kernel events exist only for eager steps (not inside a replayed graph)
     kern = len(gu_ms) > 0
-    sel = np.array(sampled, np.int64)
-    hot_bytes_gu_s = np.asarray(hot_bytes_gu, np.float64)[sel]
-    cold_bytes_s = np.asarray(cold_bytes, np.float64)[sel]
-    has_cold = cold_bytes_s > 0 if kern else None
+    hot_bytes_gu_a = np.asarray(hot_bytes_gu, np.float64)
+    has_cold = np.asarray(cold_bytes, np.float64) > 0
     mean_us = lambda v: round(float(v.mean() * 1e3), 1) if len(v) else None
-    achieved = float(hot_bytes_gu_s.sum() / (gu_ms.sum() / 1e3) / 1e9) if kern else None
+    achieved = float(hot_bytes_gu_a.sum() / (gu_ms.sum() / 1e3) / 1e9) if kern else None
+    hot_ffn_bytes = np.asarray(uh_first, np.float64) * (b13 + b2)
+    achieved_hot = (float(hot_ffn_bytes.sum() / ((gu_ms.sum() + dn_ms.sum()) / 1e3) / 1e9)
+                    if kern else None)
     value = float(np.mean(bytes_step) / (ms_per_step / 1e3) / 1e9)
-    cold_link = (float(cold_bytes_s.sum() / max(c_ms.sum() / 1e3, 1e-12) / 1e9)
+    # cold bytes of the profile pass's steps (the same calls, on the maps at its time)
+    prof_cold = np.array([account((base + i) * lps, prof_maps[((base + i) * lps) % Lr])[2]
+                          for i in range(n_prof)], np.float64) if n_prof else np.zeros(0)
+    cold_link = (float(prof_cold.sum() / max(c_ms.sum() / 1e3, 1e-12) / 1e9)
                  if len(c_ms) else None)
+    cap_hot = min(n_hot, T * k)
+    fam_gu, fam_dn = ffn_families(T, k, H, I, cap_hot)
 
     # HBM traffic of the gate/up kernel from committed rocprofv3 counter runs,
     # used only while the kernel's sources are the ones the counters were taken on
@@ -664,47 +713,83 @@ def main():
                    "weights": "mxfp4", "cold_bank": COLD_BANK[args.cold_path], "map": args.map,
                    "layer_banks_rotated": Lr, "cold_stream": not args.serial,
                    "streams": "serial" if args.serial else args.streams,
-                   "graph": bool(args.graph), "event_stride": max(1, args.event_stride),
-                   "policy": not args.no_policy},
+                   "graph": bool(args.graph), "policy": not args.no_policy,
+                   "timed_routing": "stratified" if stratify else "independent draws"},
         "us_per_layer": round(ms_per_step * 1e3 / lps, 1),
         "tokens_per_s": round(T / (ms_per_step / 1e3), 1),
+        # mean over all timed steps (wall clock) and the profile pass's
+        # per-step events (each event there adds a few us to the step)
+        "step_us": {"mean": round(ms_per_step * 1e3, 1),
+                    "profile_pass_mean": mean_us(st_ms),
+                    "profile_pass_median": (round(float(np.median(st_ms) * 1e3), 1)
+                                            if len(st_ms) else None),
+                    "profile_pass_steps": int(len(st_ms))},
         "hot_gate_up_us": mean_us(gu_ms),
         # the same launches split by whether the step staged cold rows beside them
         "hot_gate_up_us_by_step": ({"without_cold": mean_us(gu_ms[~has_cold]),
                                     "with_cold": mean_us(gu_ms[has_cold])} if kern else None),
         "hot_down_us": mean_us(dn_ms),
         "cold_ffn_us": mean_us(c_ms),
-        "hot_ffn_GBps": (round(float((np.asarray(uh_first, np.float64)[sel].sum() * (b13 + b2)) /
-                                     ((gu_ms.sum() + dn_ms.sum()) / 1e3) / 1e9), 1) if kern
-                         else None),
+        "hot_ffn_GBps": round(achieved_hot, 1) if kern else None,
+        "kernels": {"hot_gate_up": fam_gu, "hot_down": fam_dn},
         "cold_link": {"achieved_GBps": round(cold_link, 1) if cold_link is not None else None,
                       "ceiling_GBps": ceilings.get("host_link_zero_copy_read_GBps"),
                       "nominal_GBps": NOMINAL_LINK_GBPS},
         "routing": {"hot_unique_per_step": round(float(np.mean(uh_list)), 2),
                     "cold_unique_per_step": round(float(np.mean(uc_list)), 2),
+                    "cold_experts_timed": int(np.sum(uc_list)),
+                    **({"cold_experts_expected": round(
+                        strat_info["expected_cold_experts_per_call"] * K * lps, 1),
+                        "stratified": strat_info["method"]} if strat_info else {}),
                     "cold_share_of_picks": round(cold_picks / (K * lps * T * k), 4)},
         "swaps_applied": swaps, "swaps_stale": stale,
         **({"windows": windows} if (off_domain or shift) else {}),
         **({"restore": restore} if restore else {}),
         **({"refit": refit_info} if refit else {}),
-        "percentiles_us": {name: pct(v) for name, v in (("step", st_ms), ("hot_gate_up", gu_ms),
-                                                        ("hot_down", dn_ms), ("cold_path", c_ms))},
+        "percentiles_us": {name: pct(v) for name, v in (("step_profile_pass", st_ms),
+                                                        ("hot_gate_up", gu_ms),
+                                                        ("hot_down", dn_ms),
+                                                        ("cold_path_profile_pass", c_ms))},
         # host time to enqueue one step (no waiting): it must stay below the
         # step's device time for the step to measure the device
         "host_enqueue_us": {k: round(float(np.percentile(host_us, q)), 1)
                             for k, q in (("p10", 10), ("p50", 50), ("p90", 90))},
         "ceilings": ceilings,
-        "roofline": {"kernel": "ffn_gate_up_resident (hot bank)", "bound": "hbm",
+        "roofline": {"kernel": f"{fam_gu} (hot bank)", "bound": "hbm",
                      "achieved": round(achieved, 1) if kern else None, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4) if kern else None,
-                     "traffic": traffic},
+                     "traffic": traffic if fam_gu == TRAFFIC_KERNEL else None},
+        # the hot bank as a whole: gate/up + down algorithmic bytes (each
+        # touched expert's 18.8 MB once) over the two kernels' event times
+        "roofline_hot_bank": {"kernels": f"{fam_gu} + {fam_dn}", "bound": "hbm",
+                              "achieved": round(achieved_hot, 1) if kern else None,
+                              "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                              "frac": (round(achieved_hot / PEAK_HBM_GBPS, 4) if kern
+                                       else None)},
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E,
                                               b13 + b2, account, log, lps, first=base)
     print(json.dumps(result), flush=True)
+
+
+# The kernel families the library picks for a device bank (the rule of
+# launch_gate_up / launch_down in the library's ffn_mxfp4.hip, for H a
+# multiple of 1024 and aligned scale tensors), named in the result.
+TRAFFIC_KERNEL = "ffn_gate_up_resident"
+
+
+def ffn_families(T, k, H, I, cap):
+    if T >= 256:
+        return "ffn_fp4", "ffn_fp4"
+    tiled = T * k >= 2 * cap
+    gu = ("ffn_gate_up_resident" if T <= 16 and H % 1024 == 0 else
+          "ffn_tiled" if tiled else "ffn_gate_up")
+    dn = ("ffn_tiled" if tiled else
+          "ffn_down_resident" if -(-I // 256) % 6 == 0 else "ffn_down")
+    return gu, dn
 
 
 def sources_sha256(rel_paths):
@@ -901,16 +986,42 @@ def cpu_baseline_prefill(args, ids, w, layer, H, I, E, gpu_ms, log):
     dt = time.perf_counter() - t0
     per_step = dt * 4096 / n
     return {"value": round(4096 / per_step, 2), "unit": "tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle", "ms_per_step": round(per_step * 1e3, 1),
+            "kind": "oracle", "ms_per_step": round(per_step * 1e3, 1), **host_cpu_info(),
             "gpu_tokens_per_s": round(4096 / (gpu_ms / 1e3), 1),
             "sample": f"first {n} of the 4096 tokens of one timed step ({ids.size} picks, hot "
                       "and cold, plus finalize), time scaled by 4096/48"}
 
 
+def host_cpu_info():
+    """CPU model, physical cores and logical CPUs of this host, and the CPUs
+    this process may run on (from /proc/cpuinfo and the affinity mask)."""
+    model, cores, logical = None, set(), 0
+    try:
+        phys = core = None
+        for line in open("/proc/cpuinfo"):
+            key, _, val = line.partition(":")
+            key, val = key.strip(), val.strip()
+            if key == "processor":
+                logical += 1
+            elif key == "model name" and model is None:
+                model = val
+            elif key == "physical id":
+                phys = val
+            elif key == "core id":
+                core = val
+                cores.add((phys, core))
+    except OSError:
+        pass
+    return {"cpu_model": model, "physical_cores": len(cores) or None, "logical_cpus": logical,
+            "usable_cpus": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E, bexp, account, log, lps=1,
                  first=None):
     """The oracle on sampled steps of the same workload (whole layer: all picks,
-    hot and cold, plus finalize), until about 10 s of CPU time."""
+    hot and cold, plus finalize), until about 10 s of CPU time, on all the
+    threads OpenMP gives it; then on one thread, over the first picks of one
+    step (about 5 s), scaled to the whole layer."""
     import oracle
     import synth
     t_tot, b_tot, n = 0.0, 0.0, 0
@@ -931,11 +1042,30 @@ def cpu_baseline(args, ids_np, w_np, x_np, maps_host, Lr, H, I, E, bexp, account
         if t_tot > 10.0:
             break
     per = t_tot / n
-    return {"value": round(b_tot / n / per / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
+    threads = oracle.max_threads()
+    # one thread: the first tokens of the first sampled step, about 1/8 of its
+    # picks (at least one token), time scaled by picks
+    c = first * lps
+    T_all, k = ids_np.shape[1], ids_np.shape[2]
+    t1 = max(1, T_all // 8)
+    ids1 = ids_np[c][:t1]
+    U = np.unique(ids1)
+    bank = oracle.Bank(**synth.make_bank_host(U, args.seed, c % Lr, H, I))
+    rm = np.full(E, -(10 ** 6), np.int32)
+    rm[U] = np.arange(len(U), dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.moe_layer(bank, None, rm, ids1, w_np[c][:t1], x_np[c % len(x_np)][:t1], H, I,
+                     nthreads=1)
+    per1 = (time.perf_counter() - t0) * T_all / t1
+    return {"value": round(b_tot / n / per / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "us_per_layer": round(per * 1e6, 1),
-            "sample": f"{n} of the timed steps (one full layer each: all {ids_np.shape[1]} tokens x "
-                      f"{ids_np.shape[2]} picks, hot and cold, plus finalize); same weights, "
-                      "routing and activations"}
+            "us_per_layer_1core": round(per1 * 1e6, 1),
+            **host_cpu_info(),
+            "sample": f"{n} of the timed steps (one full layer each: all {T_all} tokens x "
+                      f"{k} picks, hot and cold, plus finalize; same weights, routing and "
+                      f"activations) on {threads} OpenMP threads; the 1-core figure: the first "
+                      f"{t1} tokens ({t1 * k} picks) of one step on one thread, scaled by "
+                      f"{T_all}/{t1}"}
 
 
 if __name__ == "__main__":
