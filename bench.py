@@ -82,7 +82,7 @@ def parse():
                          "the cold FFN reads the pinned host bank directly")
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "step40", "highconc", "offdomain",
-                             "domainshift", "refit"],
+                             "domainshift", "refit", "counter", "swap"],
                     help="decode: the default line (one layer of 16 tokens per step); prefill: "
                          "one 4096-token chunk per step (counter off), with the hot bank's MFMA "
                          "utilisation; step40: 40 layer calls of 7 tokens per step; highconc: "
@@ -93,7 +93,10 @@ def parse():
                          "phases), the policy following, then a restore to the boot map; refit: "
                          "the off-domain boot, a count-only profile (--profile-tokens per layer), "
                          "a map fitted off-line to those counts and applied, then timed on fresh "
-                         "traffic with no on-line policy")
+                         "traffic with no on-line policy; counter: the split kernel of 40 layers "
+                         "captured in a HIP graph, with and without the usage counter, at 6, 16 "
+                         "and 32 tokens; swap: full-size row swaps between the hot and the cold "
+                         "bank, time per swap")
     ap.add_argument("--profile-tokens", type=int, default=50_000,
                     help="refit: decode tokens counted per layer before fitting (the pages' "
                          "floor for a count profile is 50,000)")
@@ -207,6 +210,10 @@ def main():
     moe.lib()
     if args.workload == "prefill":
         return run_prefill(args)
+    if args.workload == "counter":
+        return run_counter_cost(args)
+    if args.workload == "swap":
+        return run_swap_cost(args)
     lps, off_domain, shift, refit, wname = 1, False, False, False, None
     if args.workload == "step40":
         args.tokens, lps = 7, 40
@@ -820,6 +827,141 @@ def make_layer_banks(torch, moe, synth, E, n_cold, H, I, Lr, seed, map_kind="fit
         cold.append(cb)
         maps_host.append(rm.copy())
     return hot, cold, maps_host
+
+
+def run_counter_cost(args):
+    """The counter's cost ("Should a GB300 Prefetch Its Cold Experts?", section
+    8, E1): moe_route_split for 40 layers captured in one HIP graph, once with
+    the usage counter and once without, at 6, 16 and 32 tokens per step
+    (top-6, 384 experts, each layer its own fitted map and skewed routing).
+    The two graphs are replayed alternately; the difference of their median
+    replay times is the counter's cost per 40-layer step. The counter table
+    is checked afterwards: every replay added exactly the step's histogram."""
+    import torch
+
+    import expert_weight_residency_amd as moe
+    import synth
+
+    E, k, L, seed = 384, 6, 40, args.seed
+    reps = max(50, min(args.steps, 400))
+    log = lambda m: print(m, file=sys.stderr, flush=True)
+    maps = [synth.fitted_map(E, args.cold_rows, seed, l) for l in range(L)]
+    n_hot, n_cold = E - args.cold_rows, args.cold_rows
+    maps_dev = [torch.from_numpy(m[0].copy()).cuda() for m in maps]
+    s = torch.cuda.Stream()
+    out = {}
+    for T in (6, 16, 32):
+        ids = [synth.skewed_routing(T, k, E, seed, l, 0)[0] for l in range(L)]
+        ids_d = [torch.from_numpy(i).cuda() for i in ids]
+        hs, cs = moe.Split.empty(n_hot, T, k), moe.Split.empty(n_cold, T, k)
+        ninv = torch.zeros(1, dtype=torch.int32, device="cuda")
+        counts = torch.zeros((L, E), dtype=torch.int32, device="cuda")
+
+        def body(with_counter):
+            for l in range(L):
+                moe.moe_route_split(ids_d[l], maps_dev[l], n_hot, n_cold, hs, cs, ninv,
+                                    counts[l] if with_counter else None, 256, stream=s)
+
+        graphs = {}
+        with torch.cuda.stream(s):
+            for wc in (True, False):
+                body(wc)  # eager warm-up
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    body(wc)
+                graphs[wc] = g
+            torch.cuda.synchronize()
+            counts.zero_()
+            torch.cuda.synchronize()
+            times = {True: [], False: []}
+            for r in range(reps + 10):
+                for wc in (True, False):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(s)
+                    graphs[wc].replay()
+                    b.record(s)
+                    if r >= 10:
+                        times[wc].append((a, b))
+            torch.cuda.synchronize()
+        med = {wc: float(np.median([a.elapsed_time(b) for a, b in v]) * 1e3)
+               for wc, v in times.items()}
+        hist = np.stack([np.bincount(i.ravel(), minlength=E) for i in ids])
+        exact = bool(np.array_equal(counts.cpu().numpy(), hist * (reps + 10)))
+        d = med[True] - med[False]
+        out[f"T{T}"] = {"picks_per_layer": T * k,
+                        "us_per_40_layers_with_counter": round(med[True], 1),
+                        "us_per_40_layers_without": round(med[False], 1),
+                        "counter_us_per_40_layers": round(d, 1),
+                        "counter_us_per_layer": round(d / L, 3),
+                        "share_of_14_6_ms_step_pct": round(100 * d / 14600.0, 3),
+                        "counts_exact": exact}
+        log(f"T={T}: {out[f'T{T}']}")
+    result = {"metric": "usage counter cost (split kernel, 40 layers in a HIP graph)",
+              "value": out["T16"]["counter_us_per_40_layers"], "unit": "us per 40-layer step",
+              "n_gpus": 1, "steps": reps, "warmup": 10, "higher_is_better": False,
+              "dtype": "int32", "data": "synthetic",
+              "config": {"workload": "counter_cost_split_40_layers", "experts": E, "top_k": k,
+                         "layers": L, "hot_rows": n_hot, "cold_rows": n_cold,
+                         "map": "fitted", "graph": True},
+              "by_tokens": out}
+    print(json.dumps(result), flush=True)
+
+
+def run_swap_cost(args):
+    """Full-size true swaps ("vLLM: Pin Hot Experts", "Closed, September 17
+    evening": a hot row to a staging row, the cold row into the hot slot, the
+    staging row into the cold slot, then the two-element map write) between a
+    295-row HBM bank and an 89-row pinned host bank at H = 4096, I = 2880,
+    timed one by one with events on the stream. Each swap moves one expert
+    (18.8 MB) each way over the host link and one through HBM."""
+    import torch
+
+    import expert_weight_residency_amd as moe
+    import synth
+
+    E, H, I, seed = 384, 4096, 2880, args.seed
+    n = max(8, min(args.steps, 64))
+    rm, ho, co = synth.fitted_map(E, args.cold_rows, seed, 0)
+    shapes = synth.tensor_shapes(len(ho), H, I)
+    hot = moe.Bank(*[torch.empty(s, dtype=torch.uint8, device="cuda") for s in shapes.values()])
+    synth.fill_bank_device(hot.tensors(), torch.from_numpy(ho).cuda(), seed, 0, H, I)
+    cold = moe.Bank(*[torch.empty(s, dtype=torch.uint8, pin_memory=True)
+                      for s in synth.tensor_shapes(len(co), H, I).values()], on_host=True)
+    synth.fill_bank_host(cold.tensors(), co, seed, 0, H, I)
+    rm_dev = torch.from_numpy(rm.copy()).cuda()
+    staging = torch.empty(moe.moe_expert_bytes(H, I), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    rng = np.random.default_rng(seed)
+    ev = []
+    with torch.cuda.stream(s):
+        for i in range(n + 2):
+            a, b = int(rng.integers(len(ho))), int(rng.integers(len(co)))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            moe.moe_swap_rows(hot, cold, a, b, int(ho[a]), int(co[b]), rm_dev, ho, co, staging,
+                              H, I, stream=s)
+            e1.record(s)
+            if i >= 2:
+                ev.append((e0, e1))
+        torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    eb = moe.moe_expert_bytes(H, I)
+    result = {"metric": "row swap time (full-size expert, hot HBM <-> cold pinned host)",
+              "value": round(float(np.median(us)), 1), "unit": "us per swap", "n_gpus": 1,
+              "steps": n, "warmup": 2, "higher_is_better": False, "dtype": "u8",
+              "data": "synthetic",
+              "config": {"workload": "swap_full_size", "experts": E, "hidden": H,
+                         "intermediate": I, "hot_rows": len(ho), "cold_rows": len(co),
+                         "expert_bytes": eb},
+              "us_per_swap": {"p10": round(float(np.percentile(us, 10)), 1),
+                              "p50": round(float(np.median(us)), 1),
+                              "p90": round(float(np.percentile(us, 90)), 1)},
+              "host_link_GBps_both_directions": round(2 * eb / (np.median(us) * 1e-6) / 1e9, 1),
+              "maps_equal": bool(np.array_equal(
+                  rm_dev.cpu().numpy()[np.concatenate([ho, co])],
+                  np.concatenate([np.arange(len(ho)), -1 - np.arange(len(co))])))}
+    print(json.dumps(result), flush=True)
 
 
 def run_prefill(args):

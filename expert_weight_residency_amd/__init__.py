@@ -143,7 +143,13 @@ def _need(t, name: str, nbytes: int) -> None:
 
 
 def _check_bank(bank: "Bank", H: int, I: int, name: str = "bank") -> None:
-    """Every tensor of the bank holds n_rows rows of the layout for (H, I)."""
+    """Every tensor of the bank holds n_rows rows of the layout for (H, I)
+    (remembered per bank for the tensors and sizes last checked)."""
+    key = (bank.w13.data_ptr(), bank.s13.data_ptr(), bank.w2.data_ptr(), bank.s2.data_ptr(),
+           int(bank.w13.numel()), int(bank.s13.numel()), int(bank.w2.numel()),
+           int(bank.s2.numel()), H, I)
+    if bank.__dict__.get("_sized") == key:
+        return
     R = bank.n_rows
     want = {"w13": R * 2 * I * (H // 2), "s13": R * 2 * I * (H // 32),
             "w2": R * H * (I // 2), "s2": R * H * (I // 32)}
@@ -152,6 +158,7 @@ def _check_bank(bank: "Bank", H: int, I: int, name: str = "bank") -> None:
         if got != n:
             raise MoeError(MOE_EINVAL, f"{name} {t}: {got} bytes, {R} rows at H={H}, I={I} "
                                        f"need {n}")
+    bank.__dict__["_sized"] = key
 
 
 def _check_split(split: "Split", n_rows: int, T: int, k: int, name: str = "split") -> None:

@@ -172,3 +172,61 @@ def test_refit_from_device_counts():
     print(f"refit: {len(props)} swaps, cold share {boot_share:.3f} -> {fitted_share:.3f}",
           flush=True)
     assert fitted_share < 0.25 * boot_share
+
+
+def test_five_swaps_full_expert_size():
+    """Five ordered swaps at full expert size (H = 4096, I = 2880: 18,800,640
+    bytes per expert) between a 295-row hot bank in HBM and an 89-row cold bank
+    in pinned host memory, the 384-expert fitted map of the pages' dry run
+    ("vLLM: Pin Hot Experts", "Closed, September 17 evening", E4/E4b at real
+    geometry). After each swap both swapped experts' bytes are exactly the
+    generator's bytes for those experts at the rows the map names, the rows'
+    neighbours are untouched, and the device map equals the host's. Prints the
+    time per swap (12 copies through the staging row + the map write)."""
+    Hf, If = 4096, 2880
+    rm, ho, co = synth.fitted_map(E, N_COLD, SEED, 0)
+    shapes = synth.tensor_shapes(len(ho), Hf, If)
+    hot = moe.Bank(*[torch.empty(s, dtype=torch.uint8, device="cuda") for s in shapes.values()])
+    synth.fill_bank_device(hot.tensors(), torch.from_numpy(ho).cuda(), SEED, 0, Hf, If)
+    cshapes = synth.tensor_shapes(len(co), Hf, If)
+    cold = moe.Bank(*[torch.empty(s, dtype=torch.uint8, pin_memory=True)
+                      for s in cshapes.values()], on_host=True)
+    synth.fill_bank_host(cold.tensors(), co, SEED, 0, Hf, If)
+    rm_dev = torch.from_numpy(rm.copy()).cuda()
+    rm_host = rm.copy()
+    staging = torch.empty(moe.moe_expert_bytes(Hf, If), dtype=torch.uint8, device="cuda")
+    assert staging.numel() == 18_800_640
+    torch.cuda.synchronize()
+
+    def row_bytes(e):
+        m = int(rm_host[e])
+        b, r = (hot, m) if m >= 0 else (cold, -1 - m)
+        return [getattr(b, t)[r].cpu().numpy().tobytes() for t in synth.TENSORS]
+
+    def expected(e):
+        one = synth.make_bank_host([e], SEED, 0, Hf, If)
+        return [one[t][0].tobytes() for t in synth.TENSORS]
+
+    rng = np.random.default_rng(11)
+    times = []
+    for n in range(5):
+        a, b = int(rng.integers(len(ho))), int(rng.integers(len(co)))
+        e_h, e_c = int(ho[a]), int(co[b])
+        nb_h = hot.w13[(a + 1) % len(ho)].cpu().numpy().tobytes()
+        nb_c = cold.w2[(b + 1) % len(co)].numpy().tobytes()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        moe.moe_swap_rows(hot, cold, a, b, e_h, e_c, rm_dev, ho, co, staging, Hf, If)
+        t1.record()
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1) * 1e3)
+        rm_host[e_h], rm_host[e_c] = -1 - b, a
+        assert np.array_equal(rm_dev.cpu().numpy(), rm_host), n
+        assert ho[a] == e_c and co[b] == e_h
+        assert row_bytes(e_h) == expected(e_h), (n, e_h)
+        assert row_bytes(e_c) == expected(e_c), (n, e_c)
+        assert hot.w13[(a + 1) % len(ho)].cpu().numpy().tobytes() == nb_h
+        assert cold.w2[(b + 1) % len(co)].numpy().tobytes() == nb_c
+    print(f"full-size swap: {np.round(times, 1)} us each "
+          f"({2 * 18_800_640 / (np.median(times) * 1e-6) / 1e9:.1f} GB/s over the host link "
+          "counting both directions)", flush=True)
