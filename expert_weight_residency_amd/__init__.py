@@ -23,7 +23,8 @@ MOE_MAX_TOPK = 32
 ENTRY_POINTS = ("moe_expert_bytes", "moe_ffn_workspace_bytes", "moe_route_split",
                 "moe_expert_ffn_mxfp4", "moe_expert_gate_up_mxfp4", "moe_expert_down_mxfp4",
                 "moe_stage_rows", "moe_finalize", "moe_usage_counts", "moe_swap_rows",
-                "moe_last_error")
+                "moe_last_error", "moe_expert_ffn_mxfp4_noalloc")
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class MoeError(RuntimeError):
@@ -70,6 +71,9 @@ def lib():
         L.moe_expert_ffn_mxfp4.restype = i32
         L.moe_expert_ffn_mxfp4.argtypes = [ctypes.POINTER(MoeBankC), MoeSplitC, vp, i32, i32, i32,
                                            i32, vp, vp, vp]
+        L.moe_expert_ffn_mxfp4_noalloc.restype = i32
+        L.moe_expert_ffn_mxfp4_noalloc.argtypes = [ctypes.POINTER(MoeBankC), MoeSplitC, vp, i32,
+                                                   i32, i32, i32, vp, vp]
         L.moe_expert_gate_up_mxfp4.restype = i32
         L.moe_expert_gate_up_mxfp4.argtypes = [ctypes.POINTER(MoeBankC), MoeSplitC, vp, i32, i32,
                                                i32, i32, vp, vp]
@@ -299,6 +303,24 @@ def moe_expert_ffn_mxfp4(bank: Bank, split: Split, x, k: int, I: int, workspace,
     _check(lib().moe_expert_ffn_mxfp4(ctypes.byref(b), split.abi(), _gpu(x, "x", _BF16_BITS), T, k,
                                       H, I, _gpu(workspace, "workspace"),
                                       _gpu(Y, "Y", _BF16_BITS), _stream(stream)))
+
+
+def moe_expert_ffn_mxfp4_noalloc(bank: Bank, split: Split, x, k: int, I: int, Y,
+                                 stream=None) -> None:
+    """moe_expert_ffn_mxfp4 with the library's static scratch buffer instead of
+    a workspace (allocates nothing; see the header for the size limit and the
+    sharing rule)."""
+    T, H = int(x.shape[0]), int(x.shape[1])
+    if T > 0 and bank.n_rows > 0:
+        _check_bank(bank, H, I)
+        if int(split.slots.numel()) < T * k:
+            raise MoeError(MOE_EINVAL, f"split slots: {int(split.slots.numel())} entries, "
+                                       f"need T*k = {T * k}")
+        _need(Y, "Y", 2 * T * k * H)
+    b = bank.abi()
+    _check(lib().moe_expert_ffn_mxfp4_noalloc(ctypes.byref(b), split.abi(),
+                                              _gpu(x, "x", _BF16_BITS), T, k, H, I,
+                                              _gpu(Y, "Y", _BF16_BITS), _stream(stream)))
 
 
 def moe_expert_gate_up_mxfp4(bank: Bank, split: Split, x, k: int, I: int, workspace,

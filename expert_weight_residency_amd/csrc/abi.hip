@@ -11,10 +11,15 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+int vfail(int code, const char* fmt, va_list ap) {
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  return code;
+}
+
 int fail(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  vfail(code, fmt, ap);
   va_end(ap);
   return code;
 }
@@ -73,6 +78,18 @@ int bank_device_ptrs(const moe_bank* b, const uint8_t* out[4]) {
 }
 
 }  // namespace
+
+namespace moe {
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(code, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+}  // namespace moe
 
 extern "C" {
 
@@ -138,6 +155,29 @@ static int ffn_prepare(const moe_bank* bank, const moe_split& split, const void*
   return MOE_OK;
 }
 
+}  // extern "C"
+
+namespace moe {
+
+int expert_ffn(const moe_bank* bank, const moe_split& split, const uint16_t* x, int T, int k,
+               int H, int I, void* workspace, uint16_t* Y, void* stream) {
+  const uint8_t* p[4];
+  int cap = 0, rc;
+  bool skip;
+  if ((rc = ffn_prepare(bank, split, x, T, k, H, I, workspace, Y, p, &cap, &skip))) return rc;
+  if (skip) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* h = static_cast<uint16_t*>(workspace);
+  hipError_t e = launch_gate_up(p[0], p[1], cap, bank->on_host, split, x, T, k, H, I, h, s);
+  if (e == hipSuccess) e = launch_down(p[2], p[3], cap, bank->on_host, split, T, k, H, I, h, Y, s);
+  if (e != hipSuccess) return fail(MOE_EHIP, "expert FFN launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace moe
+
+extern "C" {
+
 int moe_expert_gate_up_mxfp4(const moe_bank* bank, moe_split split, const uint16_t* x, int T,
                              int k, int H, int I, void* workspace, void* stream) {
   const uint8_t* p[4];
@@ -171,17 +211,7 @@ int moe_expert_down_mxfp4(const moe_bank* bank, moe_split split, int T, int k, i
 
 int moe_expert_ffn_mxfp4(const moe_bank* bank, moe_split split, const uint16_t* x, int T, int k,
                          int H, int I, void* workspace, uint16_t* Y, void* stream) {
-  const uint8_t* p[4];
-  int cap = 0, rc;
-  bool skip;
-  if ((rc = ffn_prepare(bank, split, x, T, k, H, I, workspace, Y, p, &cap, &skip))) return rc;
-  if (skip) return ok();
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t* h = static_cast<uint16_t*>(workspace);
-  hipError_t e = moe::launch_gate_up(p[0], p[1], cap, bank->on_host, split, x, T, k, H, I, h, s);
-  if (e == hipSuccess) e = moe::launch_down(p[2], p[3], cap, bank->on_host, split, T, k, H, I, h, Y, s);
-  if (e != hipSuccess) return fail(MOE_EHIP, "expert FFN launch: %s", hipGetErrorString(e));
-  return ok();
+  return moe::expert_ffn(bank, split, x, T, k, H, I, workspace, Y, stream);
 }
 
 int moe_stage_rows(const moe_bank* src, moe_split split, int T, int k, const moe_bank* dst,

@@ -119,6 +119,14 @@ hipError_t launch_finalize(const uint16_t* Y, const float* w, int T, int k, int 
 hipError_t launch_map_write(int32_t* row_map, int e_a, int v_a, int e_b, int v_b,
                             hipStream_t stream);
 
+// The body of moe_expert_ffn_mxfp4 (argument checks, then gate/up and down
+// on `stream` with `workspace` as their scratch), shared with the entry point
+// that takes no workspace; and the thread-local error message setter of the
+// entry points (returns `code`).
+int expert_ffn(const moe_bank* bank, const moe_split& split, const uint16_t* x, int T, int k,
+               int H, int I, void* workspace, uint16_t* Y, void* stream);
+int set_error(int code, const char* fmt, ...);
+
 // Longest reduction axis (H or I) the expert FFN supports (one token row must
 // fit its LDS activation tile).
 int ffn_max_reduction();

@@ -176,6 +176,31 @@ int moe_route_split(const int32_t *topk_ids, int T, int k, const int32_t *row_ma
 int moe_expert_ffn_mxfp4(const moe_bank *bank, moe_split split, const uint16_t *x, int T, int k,
                          int H, int I, void *workspace, uint16_t *Y, void *stream);
 
+/* Bytes of the static device scratch buffer moe_expert_ffn_mxfp4_noalloc
+ * uses in place of a workspace (32 MiB per device). */
+#define MOE_NOALLOC_SCRATCH_BYTES (32 << 20)
+
+/*
+ * moe_expert_ffn_mxfp4_noalloc -- moe_expert_ffn_mxfp4 for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * The same operation, kernels and bits as moe_expert_ffn_mxfp4 with the same
+ * arguments, but the intermediate rows live in one static device buffer of
+ * MOE_NOALLOC_SCRATCH_BYTES per device, owned by the library and held until
+ * the process ends, instead of a workspace argument. Steps whose
+ * moe_ffn_workspace_bytes(T, k, H, I) exceeds that size are refused with
+ * MOE_EINVAL before anything is enqueued (at H = 4096, I = 2880, top-6: every
+ * step below MOE_FP4_MIN_TOKENS tokens, and prefill steps up to 378 tokens).
+ * The buffer's device address is taken on the first call on each device
+ * (hipGetSymbolAddress, no allocation). Every call on one device shares that
+ * device's buffer: calls that overlap on one GPU race, except the two bank
+ * calls of one step (the same T, k, H and I), which write disjoint slots of it.
+ * Nothing in the buffer needs clearing between calls.
+ */
+int moe_expert_ffn_mxfp4_noalloc(const moe_bank *bank, moe_split split, const uint16_t *x, int T,
+                                 int k, int H, int I, uint16_t *Y, void *stream);
+
 /*
  * moe_expert_gate_up_mxfp4 / moe_expert_down_mxfp4 -- the two launches of
  * moe_expert_ffn_mxfp4, callable one at a time (for timing each kernel, or to
