@@ -4,7 +4,7 @@
 Workload (default): one full-shape routed MoE layer per step -- 384 experts,
 top-6, hidden 4096, intermediate 2880 (one MXFP4 expert = 18,800,640 B), 16
 decode tokens, 295 hot expert rows in HBM and 89 cold rows in pinned host
-memory read in place, a residency map fitted to the routing distribution
+memory read in place (--cold-path), a residency map fitted to the routing distribution
 (about 1.7% of picks cold), skewed synthetic routing shaped after the pages'
 decode histogram. Steps rotate through --layers distinct layer banks and use
 fresh routing and activations each step, so the 256 MB Infinity Cache cannot
@@ -76,10 +76,12 @@ def parse():
                     help="decode: which bank's FFN goes on the second stream (the other stays "
                          "on the main stream with the split and the finalize)")
     ap.add_argument("--seed", type=int, default=20260917)
-    ap.add_argument("--cold-path", default="staged", choices=["staged", "inplace"],
-                    help="staged: copy the step's active cold rows into HBM with one contiguous "
-                         "stream each (moe_stage_rows), then run the cold FFN from HBM; inplace: "
-                         "the cold FFN reads the pinned host bank directly")
+    ap.add_argument("--cold-path", default="inplace", choices=["staged", "inplace"],
+                    help="inplace: the cold FFN reads the pinned host bank directly (the pages' "
+                         "method; at decode sizes each item's bytes cross the link as one "
+                         "linear stream into LDS); staged: copy the step's active cold rows into "
+                         "HBM with one contiguous stream each (moe_stage_rows), then run the "
+                         "cold FFN from HBM")
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "step40", "highconc", "offdomain",
                              "domainshift", "refit", "counter", "swap"],

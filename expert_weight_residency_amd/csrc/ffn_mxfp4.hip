@@ -273,6 +273,8 @@ hipError_t launch_gate_up(const uint8_t* w13, const uint8_t* s13, int cap, int o
                           uint16_t* h_ws, hipStream_t stream) {
   if (ffn_use_fp4(T))
     return launch_gate_up_fp4(w13, s13, cap, on_host, sp, x, T, k, H, I, h_ws, stream);
+  if (on_host && ffn_use_gate_up_host(T, k, H, I, s13))
+    return launch_gate_up_host(w13, s13, sp, T, k, H, I, x, h_ws, stream);
   if (ffn_use_resident(T, k, H, cap, s13))
     return launch_gate_up_resident(w13, s13, cap, on_host, sp, x, T, k, H, I, h_ws, stream);
   if (ffn_use_tiled(T, k, cap))
@@ -292,6 +294,8 @@ hipError_t launch_down(const uint8_t* w2, const uint8_t* s2, int cap, int on_hos
                        uint16_t* Y, hipStream_t stream) {
   if (ffn_use_fp4(T))
     return launch_down_fp4(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
+  if (on_host && ffn_use_down_host(T, k, H, I, s2))
+    return launch_down_host(w2, s2, sp, T, k, H, I, h_ws, Y, stream);
   if (ffn_use_tiled(T, k, cap))
     return launch_down_tiled(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
   if (ffn_use_down_resident(T, k, H, I, s2))

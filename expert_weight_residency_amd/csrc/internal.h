@@ -88,6 +88,21 @@ constexpr int kTiledMinPicksPerRow = 2;
 constexpr int kTiledHostWaves = 64;
 bool ffn_use_tiled(int T, int k, int cap);
 
+// Host-bank kernels for decode-sized steps (ffn_host.hip): each work item's
+// weights are copied from pinned host memory into LDS in the linear pattern
+// the host link streams fastest, then multiplied from there. Steps of at most
+// kHostMaxTokens tokens, a bank in host memory; same bits as the other bf16
+// families.
+constexpr int kHostMaxTokens = 16;
+bool ffn_use_gate_up_host(int T, int k, int H, int I, const void* s13);
+hipError_t launch_gate_up_host(const uint8_t* w13, const uint8_t* s13, const moe_split& split,
+                               int T, int k, int H, int I, const uint16_t* x, uint16_t* h_ws,
+                               hipStream_t stream);
+bool ffn_use_down_host(int T, int k, int H, int I, const void* s2);
+hipError_t launch_down_host(const uint8_t* w2, const uint8_t* s2, const moe_split& split, int T,
+                            int k, int H, int I, const uint16_t* h_ws, uint16_t* Y,
+                            hipStream_t stream);
+
 // Steps of at least kFp4MinTokens tokens (prefill) run both GEMMs on the
 // block-scaled FP4 matrix instruction (ffn_fp4.hip), for every bank: the choice
 // depends on the step only, so split and unsplit steps take the same path.
