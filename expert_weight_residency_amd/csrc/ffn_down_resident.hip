@@ -4,18 +4,18 @@
 // active row r ("vLLM: Pin Hot Experts", section "Results, September 17": the
 // routed MXFP4 expert FFN per bank, unweighted rows for a later finalize).
 //
-//  - One workgroup of 16 wavefronts per CU (for a device bank on all CUs but
+//  - One workgroup of 8 wavefronts per CU (for a device bank on all CUs but
 //    the few a host-bank launch beside it holds; for a bank in host memory on
 //    those few). Work item = kNG groups of 16 output rows of one active expert.
 //    Items are ordered (expert, row block); workgroup b takes one contiguous
 //    run of them (equal runs over all workgroups, so every CU has work), so a
 //    workgroup touches one or two experts (a few at small H), and its
 //    wavefronts take the run's items one at a time from a counter in LDS. (A
-//    SIMD issues for its oldest wavefront first: with fixed equal shares its
-//    four wavefronts finish one after another, ~47, 68, 93 and 105 us into a
-//    decode step, and the last quarter of the time runs with a quarter of the
-//    loads in flight. Taking items as they go, the wavefronts finish within
-//    about one item of each other.)
+//    SIMD issues for its oldest wavefront first: with fixed equal shares (16
+//    wavefronts per CU at the time) its wavefronts finished one after another,
+//    ~47, 68, 93 and 105 us into a decode step, the last quarter of the time
+//    with a quarter of the loads in flight. Taking items as they go, the
+//    wavefronts finish within about one item of each other.)
 //  - The down GEMM's B operand is h, one row per slot, so unlike gate/up the
 //    activations are not shared by every workgroup. Each workgroup stages the
 //    h rows of the slots of its experts into LDS (zero-padded to whole
@@ -51,10 +51,17 @@ namespace {
 
 using namespace mx;
 
-constexpr int kWaves = 16;
+// 8 wavefronts with 2 chunks each in flight: a sweep of the decode step at
+// H = 4096, I = 2880 (hot bank alone, us per launch; wavefronts x chunks):
+// 16x5 92.8, 16x2 90.1, 12x5 91.5, 12x2 89.6, 10x2 89.3, 8x5 88.4, 8x3 87.4,
+// 8x2 86.2, 8x1 86.3, 6x3 86.0, 6x2 85.6, 4x5 94.8, 4x11 96.6, 8x11 91.8.
+// More requests in flight than the CU needs to keep its share of HBM busy
+// only evict, between the two chunks that read it, the line a 1440-byte row
+// shares with its neighbour (with the streaming cache policy 16x5 takes 104.9).
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kNG = 1;    // 16-row MFMA groups per item
-constexpr int kP = 5;     // weight chunks in flight per wavefront (ring of kP + 1)
+constexpr int kP = 2;     // weight chunks in flight per wavefront (ring of kP + 1)
 constexpr int kSbl = 2;   // 16-byte scale granules per lane per item (covers I <= 4096 / kNG)
 constexpr size_t kLdsMax = 160 * 1024;  // gfx950: the LDS of one CU
 
@@ -71,7 +78,7 @@ __host__ __device__ inline Shape shape_of(int I) {
   return s;
 }
 
-// LDS: h rows [max_rows][kpad] bf16 | per-wavefront scale slots [16][sbw] |
+// LDS: h rows [max_rows][kpad] bf16 | per-wavefront scale slots [kWaves][sbw] |
 // slot ids of the staged rows [max_rows].
 __host__ __device__ inline size_t lds_bytes(const Shape& s, int max_rows) {
   return (size_t)max_rows * s.kpad * 2 + (size_t)kWaves * s.sbw + (size_t)max_rows * 4;
