@@ -146,7 +146,9 @@ int set_error(int code, const char* fmt, ...);
 // fit its LDS activation tile).
 int ffn_max_reduction();
 
-// Largest pick count handled by the single-kernel split.
-constexpr int kSplitSingleMaxPicks = 2048;
+// Largest pick count handled by the single-kernel split (its slot placement
+// compares each pick with every earlier one; above this a second kernel
+// places the slots by row).
+constexpr int kSplitSingleMaxPicks = 512;
 
 }  // namespace moe

@@ -134,7 +134,7 @@ size_t moe_ffn_workspace_bytes(int T, int k, int H, int I);
  * topk_ids: device int32 [T][k]. row_map: device int32 [E]. n_hot_rows /
  * n_cold_rows: bank sizes (either may be 0; its split must then still be
  * valid buffers of capacity 0 plus n_active and row_off[1]). n_invalid:
- * device int32 [1]. Launches one kernel when T*k <= 2048, two otherwise.
+ * device int32 [1]. Launches one kernel when T*k <= 512, two otherwise.
  */
 int moe_route_split(const int32_t *topk_ids, int T, int k, const int32_t *row_map, int E,
                     int n_hot_rows, int n_cold_rows, int32_t *counts_layer, int count_tmax,
