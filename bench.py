@@ -76,12 +76,14 @@ def parse():
                     help="decode: which bank's FFN goes on the second stream (the other stays "
                          "on the main stream with the split and the finalize)")
     ap.add_argument("--seed", type=int, default=20260917)
-    ap.add_argument("--cold-path", default="inplace", choices=["staged", "inplace"],
+    ap.add_argument("--cold-path", default=None, choices=["staged", "inplace"],
                     help="inplace: the cold FFN reads the pinned host bank directly (the pages' "
                          "method; at decode sizes each item's bytes cross the link as one "
                          "linear stream into LDS); staged: copy the step's active cold rows into "
                          "HBM with one contiguous stream each (moe_stage_rows), then run the "
-                         "cold FFN from HBM")
+                         "cold FFN from HBM. Default: inplace for decode steps, staged for the "
+                         "prefill workload (its FP4 kernel reads host memory at ~40 GB/s in "
+                         "place, the copy runs at the link's ~55 GB/s)")
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "step40", "highconc", "offdomain",
                              "domainshift", "refit", "counter", "swap"],
@@ -210,6 +212,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.lib()
+    if args.cold_path is None:
+        args.cold_path = "staged" if args.workload == "prefill" else "inplace"
     if args.workload == "prefill":
         return run_prefill(args)
     if args.workload == "counter":

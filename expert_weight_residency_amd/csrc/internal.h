@@ -148,7 +148,7 @@ int ffn_max_reduction();
 
 // Largest pick count handled by the single-kernel split (its slot placement
 // compares each pick with every earlier one; above this a second kernel
-// places the slots by row).
+// places the slots with a stable counting scatter).
 constexpr int kSplitSingleMaxPicks = 512;
 
 }  // namespace moe
