@@ -81,9 +81,9 @@ def parse():
                          "method; at decode sizes each item's bytes cross the link as one "
                          "linear stream into LDS); staged: copy the step's active cold rows into "
                          "HBM with one contiguous stream each (moe_stage_rows), then run the "
-                         "cold FFN from HBM. Default: inplace for decode steps, staged for the "
-                         "prefill workload (its FP4 kernel reads host memory at ~40 GB/s in "
-                         "place, the copy runs at the link's ~55 GB/s)")
+                         "cold FFN from HBM. Default: inplace for steps of at most 16 tokens, "
+                         "staged above (the kernels for larger steps read host memory at "
+                         "~40 GB/s in place; the copy runs at the link's ~55 GB/s)")
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "step40", "highconc", "offdomain",
                              "domainshift", "refit", "counter", "swap"],
@@ -212,7 +212,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     moe.lib()
-    if args.cold_path is None:
+    cold_path_default = args.cold_path is None
+    if cold_path_default:
         args.cold_path = "staged" if args.workload == "prefill" else "inplace"
     if args.workload == "prefill":
         return run_prefill(args)
@@ -247,6 +248,10 @@ def main():
         args.steps, args.warmup = min(args.steps, 256), min(args.warmup, 8)
         args.no_policy = True
         wname = f"refit_off_domain_decode_t7_{args.layers}_layers"
+    if cold_path_default and args.tokens > HOST_KERNEL_MAX_TOKENS:
+        # above 16 tokens the in-place cold FFN runs the operand-layout kernels,
+        # which read host memory at ~40 GB/s; the staging copy runs at the link rate
+        args.cold_path = "staged"
     E, k, H, I, T = 384, 6, 4096, 2880, args.tokens
     routing = args.routing
     if routing == "auto":
@@ -792,6 +797,9 @@ def main():
 # launch_gate_up / launch_down in the library's ffn_mxfp4.hip, for H a
 # multiple of 1024 and aligned scale tensors), named in the result.
 TRAFFIC_KERNEL = "ffn_gate_up_resident"
+# the largest step for which a bank in host memory runs the linear-read host
+# kernels (kHostMaxTokens in the library)
+HOST_KERNEL_MAX_TOKENS = 16
 
 
 def ffn_families(T, k, H, I, cap):
