@@ -53,7 +53,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer µs/decode step + achieved HBM GB/s (384e top-6 MXFP4, 1 GPU)"
 PEAK_HBM_GBPS = 8000.0
-COLD_BANK = {"inplace": "pinned_host_in_place", "staged": "pinned_host_staged_to_hbm"}
+COLD_BANK = {"inplace": "pinned_host_in_place", "staged": "pinned_host_staged_to_hbm",
+             "dma": "pinned_host_dma_copied_to_hbm"}
 NOMINAL_LINK_GBPS = 63.0
 
 
@@ -76,14 +77,16 @@ def parse():
                     help="decode: which bank's FFN goes on the second stream (the other stays "
                          "on the main stream with the split and the finalize)")
     ap.add_argument("--seed", type=int, default=20260917)
-    ap.add_argument("--cold-path", default=None, choices=["staged", "inplace"],
+    ap.add_argument("--cold-path", default=None, choices=["staged", "inplace", "dma"],
                     help="inplace: the cold FFN reads the pinned host bank directly (the pages' "
                          "method; at decode sizes each item's bytes cross the link as one "
                          "linear stream into LDS); staged: copy the step's active cold rows into "
                          "HBM with one contiguous stream each (moe_stage_rows), then run the "
                          "cold FFN from HBM. Default: inplace for steps of at most 16 tokens, "
                          "staged above (the kernels for larger steps read host memory at "
-                         "~40 GB/s in place; the copy runs at the link's ~55 GB/s)")
+                         "~40 GB/s in place; the copy runs at the link's ~55 GB/s). dma: "
+                         "the staging copy by the DMA engines (moe_stage_rows_dma) from the "
+                         "active rows read back to the host after the split")
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "step40", "highconc", "offdomain",
                              "domainshift", "refit", "counter", "swap"],
@@ -248,6 +251,8 @@ def main():
         args.steps, args.warmup = min(args.steps, 256), min(args.warmup, 8)
         args.no_policy = True
         wname = f"refit_off_domain_decode_t7_{args.layers}_layers"
+    if args.cold_path == "dma" and args.graph:
+        sys.exit("--cold-path dma reads the split back to the host every step: not capturable")
     if cold_path_default and args.tokens > HOST_KERNEL_MAX_TOKENS:
         # above 16 tokens the in-place cold FFN runs the operand-layout kernels,
         # which read host memory at ~40 GB/s; the staging copy runs at the link rate
@@ -359,7 +364,8 @@ def main():
     w_d = torch.from_numpy(w_np).cuda()
     x_d = torch.from_numpy(x_np.view(np.int16)).cuda()
     bufs = LayerBuffers.allocate(T, k, H, I, n_hot, n_cold)
-    stage = ColdStage(min(n_cold, T * k), H, I) if args.cold_path == "staged" else None
+    stage = (ColdStage(min(n_cold, T * k), H, I, dma=args.cold_path == "dma")
+             if args.cold_path in ("staged", "dma") else None)
     main_s = torch.cuda.Stream()
     side_s = main_s if args.serial else torch.cuda.Stream()
     # --streams cold-side: the cold path on the side stream; hot-side: the hot
@@ -1013,7 +1019,8 @@ def run_prefill(args):
     ids_d = torch.from_numpy(ids_np).cuda()
     w_d = torch.from_numpy(w_np).cuda()
     bufs = LayerBuffers.allocate(T, k, H, I, n_hot, n_cold)
-    stage = ColdStage(min(n_cold, T * k), H, I) if args.cold_path == "staged" else None
+    stage = (ColdStage(min(n_cold, T * k), H, I, dma=args.cold_path == "dma")
+             if args.cold_path in ("staged", "dma") else None)
     main_s = torch.cuda.Stream()
     cold_s = main_s if args.serial else torch.cuda.Stream()
     torch.cuda.synchronize()

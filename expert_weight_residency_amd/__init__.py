@@ -23,7 +23,7 @@ MOE_MAX_TOPK = 32
 ENTRY_POINTS = ("moe_expert_bytes", "moe_ffn_workspace_bytes", "moe_route_split",
                 "moe_expert_ffn_mxfp4", "moe_expert_gate_up_mxfp4", "moe_expert_down_mxfp4",
                 "moe_stage_rows", "moe_finalize", "moe_usage_counts", "moe_swap_rows",
-                "moe_last_error", "moe_expert_ffn_mxfp4_noalloc")
+                "moe_last_error", "moe_expert_ffn_mxfp4_noalloc", "moe_stage_rows_dma")
 MOE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -83,6 +83,9 @@ def lib():
         L.moe_stage_rows.restype = i32
         L.moe_stage_rows.argtypes = [ctypes.POINTER(MoeBankC), MoeSplitC, i32, i32,
                                      ctypes.POINTER(MoeBankC), vp, i32, i32, i32, vp]
+        L.moe_stage_rows_dma.restype = i32
+        L.moe_stage_rows_dma.argtypes = [ctypes.POINTER(MoeBankC), vp, i32,
+                                         ctypes.POINTER(MoeBankC), i32, i32, i32, vp]
         L.moe_finalize.restype = i32
         L.moe_finalize.argtypes = [vp, vp, i32, i32, i32, vp, vp]
         L.moe_usage_counts.restype = i32
@@ -361,6 +364,21 @@ def moe_stage_rows(src: Bank, split: Split, T: int, k: int, dst: Bank, dst_rows,
                                 _gpu(dst_rows, "dst_rows", ("torch.int32",)), H, I, int(parts),
                                 _stream(stream)))
     return Split(split.n_active, dst_rows, split.row_off, split.slots)
+
+
+def moe_stage_rows_dma(src: Bank, rows, dst: Bank, H: int, I: int, parts: int = STAGE_ALL,
+                       stream=None) -> None:
+    """Copy rows[a] of src's tensors that `parts` names to row a of the device
+    bank dst with the DMA engines; rows: host int32 (a CPU tensor or array)."""
+    import numpy as np
+    r = np.ascontiguousarray(rows.cpu().numpy() if hasattr(rows, "cpu") else rows, dtype=np.int32)
+    n = int(r.shape[0])
+    if n > 0:
+        _check_bank(src, H, I, "src")
+        _check_bank(dst, H, I, "dst")
+    s, d = src.abi(), dst.abi()
+    _check(lib().moe_stage_rows_dma(ctypes.byref(s), r.ctypes.data if n else None, n,
+                                    ctypes.byref(d), H, I, int(parts), _stream(stream)))
 
 
 def moe_finalize(Y, topk_w, out, stream=None) -> None:

@@ -252,6 +252,52 @@ int moe_stage_rows(const moe_bank* src, moe_split split, int T, int k, const moe
   return ok();
 }
 
+int moe_stage_rows_dma(const moe_bank* src, const int32_t* rows, int n, const moe_bank* dst,
+                       int H, int I, int parts, void* stream) {
+  int rc;
+  if (parts < MOE_STAGE_GATE_UP || parts > MOE_STAGE_ALL)
+    return fail(MOE_EINVAL, "parts=%d must be 1 (gate/up), 2 (down) or 3 (both)", parts);
+  if (n < 0) return fail(MOE_EINVAL, "n=%d must be >= 0", n);
+  if (H <= 0 || H % 64 || I <= 0 || I % 64) return fail(MOE_EINVAL, "H, I must be multiples of 64");
+  if (!src || !dst) return fail(MOE_EINVAL, "src and dst must not be NULL");
+  if (src->n_rows < 0 || src->n_rows > MOE_MAX_ROWS)
+    return fail(MOE_EINVAL, "src rows %d outside [0, %d]", src->n_rows, MOE_MAX_ROWS);
+  if (n == 0) return ok();
+  if (!rows) return fail(MOE_EINVAL, "rows must not be NULL");
+  if (dst->on_host) return fail(MOE_EINVAL, "dst must be a device bank (on_host = 0)");
+  if (dst->n_rows < n) return fail(MOE_EINVAL, "dst holds %d rows, %d are named", dst->n_rows, n);
+  for (int a = 0; a < n; ++a)
+    if (rows[a] < 0 || rows[a] >= src->n_rows)
+      return fail(MOE_EINVAL, "rows[%d]=%d outside [0, %d)", a, rows[a], src->n_rows);
+  const uint8_t* sp[4];
+  const uint8_t* dq[4];
+  if ((rc = bank_device_ptrs(src, sp)) || (rc = bank_device_ptrs(dst, dq))) return rc;
+  const uint8_t* const sh[4] = {static_cast<const uint8_t*>(src->w13),
+                                static_cast<const uint8_t*>(src->s13),
+                                static_cast<const uint8_t*>(src->w2),
+                                static_cast<const uint8_t*>(src->s2)};
+  const bool gu = parts & MOE_STAGE_GATE_UP, dn = parts & MOE_STAGE_DOWN;
+  const uint64_t rb[4] = {gu ? (uint64_t)2 * I * (H / 2) : 0, gu ? (uint64_t)2 * I * (H / 32) : 0,
+                          dn ? (uint64_t)H * (I / 2) : 0, dn ? (uint64_t)H * (I / 32) : 0};
+  const hipMemcpyKind kind = src->on_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // one copy per run of consecutive source rows (they land on consecutive
+  // destination rows), per tensor
+  for (int a = 0; a < n;) {
+    int b = a + 1;
+    while (b < n && rows[b] == rows[b - 1] + 1) ++b;
+    for (int t = 0; t < 4; ++t) {
+      if (!rb[t]) continue;
+      const hipError_t e =
+          hipMemcpyAsync(const_cast<uint8_t*>(dq[t]) + (uint64_t)a * rb[t],
+                         sh[t] + (uint64_t)rows[a] * rb[t], (uint64_t)(b - a) * rb[t], kind, st);
+      if (e != hipSuccess) return fail(MOE_EHIP, "stage rows copy: %s", hipGetErrorString(e));
+    }
+    a = b;
+  }
+  return ok();
+}
+
 int moe_finalize(const uint16_t* Y, const float* topk_w, int T, int k, int H, uint16_t* out,
                  void* stream) {
   if (T < 0) return fail(MOE_EINVAL, "T=%d must be >= 0", T);

@@ -3,7 +3,8 @@
 Holds the two banks, the device row map and the preallocated split, workspace
 and output buffers for a given token count, and issues, per step:
 moe_route_split -> moe_expert_ffn_mxfp4 (hot) -> moe_expert_ffn_mxfp4 (cold,
-optionally after moe_stage_rows into an HBM stage) -> moe_finalize ("vLLM: Pin
+optionally after moe_stage_rows, or moe_stage_rows_dma, into an HBM stage) ->
+moe_finalize ("vLLM: Pin
 Hot Experts", section "Results, September 17": split the ids by residency, one
 routed call per bank without finalization, one ordered finalize). The cold
 call may run on a second stream (and, with a stage, its gate/up GEMM beside
@@ -19,7 +20,7 @@ import torch
 
 from . import (STAGE_ALL, STAGE_DOWN, STAGE_GATE_UP, Bank, Split, moe_expert_down_mxfp4,
                moe_expert_ffn_mxfp4, moe_expert_gate_up_mxfp4, moe_ffn_workspace_bytes,
-               moe_finalize, moe_route_split, moe_stage_rows)
+               moe_finalize, moe_route_split, moe_stage_rows, moe_stage_rows_dma)
 
 
 @dataclass
@@ -44,14 +45,24 @@ class LayerBuffers:
 class ColdStage:
     """A device bank the step's active cold rows are copied into before the
     cold FFN (moe_stage_rows), with its row list. Rows: at least min(cold
-    rows, T*k) of the largest step; one stage can serve every layer in turn."""
+    rows, T*k) of the largest step; one stage can serve every layer in turn.
+    dma: copy with the DMA engines (moe_stage_rows_dma) from a row list read
+    back to the host after the split, instead of the copy kernel."""
 
-    def __init__(self, n_rows: int, H: int, I: int, device="cuda"):
+    def __init__(self, n_rows: int, H: int, I: int, device="cuda", dma: bool = False):
+        self.dma = dma
+        if dma:
+            # the DMA copy needs the active rows on the host: read back after
+            # the split into pinned buffers; the staged split's row list is
+            # then 0 .. n-1 once and for all
+            self.n_host = torch.zeros(1, dtype=torch.int32, pin_memory=True)
+            self.rows_host = torch.zeros(max(n_rows, 1), dtype=torch.int32, pin_memory=True)
         shapes = {"w13": (n_rows, 2 * I, H // 2), "s13": (n_rows, 2 * I, H // 32),
                   "w2": (n_rows, H, I // 2), "s2": (n_rows, H, I // 32)}
         t = {k: torch.empty(sh, dtype=torch.uint8, device=device) for k, sh in shapes.items()}
         self.bank = Bank(t["w13"], t["s13"], t["w2"], t["s2"], on_host=False)
-        self.rows = torch.zeros(max(n_rows, 1), dtype=torch.int32, device=device)
+        self.rows = (torch.arange(max(n_rows, 1), dtype=torch.int32, device=device) if dma else
+                     torch.zeros(max(n_rows, 1), dtype=torch.int32, device=device))
         # runs the FFN on the stage while the copy is still going (see
         # enqueue_cold_ffn), with the two events that order it (re-recorded
         # every call: a wait takes the record before it)
@@ -73,6 +84,23 @@ def enqueue_cold_ffn(cold: Bank, split: Split, x, k: int, H: int, I: int, bufs: 
         moe_expert_ffn_mxfp4(cold, split, x, k, I, bufs.workspace, bufs.Y, stream=stream)
         return stream
     T = int(x.shape[0])
+    if stage.dma:
+        # copy-on-miss by the DMA engines: the split's active cold rows come
+        # back to the host (this waits for the split), then one copy per run of
+        # consecutive rows per tensor
+        cap = min(cold.n_rows, T * k)
+        if cap == 0:
+            return stream
+        with torch.cuda.stream(stream):
+            stage.n_host.copy_(split.n_active[:1], non_blocking=True)
+            stage.rows_host[:cap].copy_(split.active_rows[:cap], non_blocking=True)
+        stream.synchronize()
+        n = int(stage.n_host[0])
+        moe_stage_rows_dma(cold, stage.rows_host[:n], stage.bank, H, I, parts=STAGE_ALL,
+                           stream=stream)
+        staged = Split(split.n_active, stage.rows, split.row_off, split.slots)
+        moe_expert_ffn_mxfp4(stage.bank, staged, x, k, I, bufs.workspace, bufs.Y, stream=stream)
+        return stream
     if not overlap:
         staged = moe_stage_rows(cold, split, T, k, stage.bank, stage.rows, H, I,
                                 parts=STAGE_ALL, stream=stream)

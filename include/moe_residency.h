@@ -247,6 +247,28 @@ int moe_stage_rows(const moe_bank *src, moe_split split, int T, int k, const moe
                    int32_t *dst_rows, int H, int I, int parts, void *stream);
 
 /*
+ * moe_stage_rows_dma -- the copy of moe_stage_rows by the DMA engines, for a
+ * row list the host holds ("Should a GB300 Prefetch Its Cold Experts?": copy
+ * a cold expert into HBM on a miss instead of reading it in place).
+ *
+ * For a = 0 .. n-1: row rows[a] of each tensor of `src` that `parts` names is
+ * copied to row a of the same tensor of `dst` with hipMemcpyAsync on `stream`
+ * (one copy per run of consecutive rows per tensor); no compute unit takes
+ * part. With rows = the split's active rows (read back to the host after
+ * moe_route_split) and a device row list 0 .. n-1 in place of
+ * split.active_rows, moe_expert_ffn_mxfp4 on `dst` gives the same results as
+ * on `src`.
+ *
+ * src: host or device bank. rows: host int32 [n], each in [0, src->n_rows).
+ * dst: a device bank with n_rows >= n. parts as for moe_stage_rows. Every
+ * argument is checked before any copy is enqueued (MOE_EINVAL); MOE_EHIP if
+ * the runtime refuses a copy (copies enqueued before it stay enqueued).
+ * Nothing is enqueued when n == 0.
+ */
+int moe_stage_rows_dma(const moe_bank *src, const int32_t *rows, int n, const moe_bank *dst,
+                       int H, int I, int parts, void *stream);
+
+/*
  * moe_finalize -- ordered fp32 FMA combine of the k rows of each token.
  *
  * out[t][o] = bf16_rne(acc) with acc = +0.0f and, for j = 0 .. k-1 in the

@@ -109,6 +109,38 @@ def test_stage_rows_rejects_bad_args(L):
     assert call(src_=moe.MoeBankC(p, p, p, p, 0, 0)) == moe.MOE_OK
 
 
+def test_stage_rows_dma_rejects_bad_args(L):
+    """Argument errors of moe_stage_rows_dma come back before any copy is
+    enqueued (device banks: no pointer translation either)."""
+    p = 0x1000
+    src = moe.MoeBankC(p, p, p, p, 10, 0)
+    dst = moe.MoeBankC(p, p, p, p, 4, 0)
+
+    def call(rows, n=None, src_=src, dst_=dst, H=256, I=128, parts=moe.STAGE_ALL):
+        r = np.ascontiguousarray(rows, dtype=np.int32)
+        return L.moe_stage_rows_dma(ctypes.byref(src_) if src_ is not None else None,
+                                    r.ctypes.data if r.size else None,
+                                    len(r) if n is None else n,
+                                    ctypes.byref(dst_) if dst_ is not None else None, H, I,
+                                    parts, None)
+
+    for parts in (0, 4, -1):
+        assert call([1, 2], parts=parts) == moe.MOE_EINVAL
+        assert "parts" in moe.moe_last_error()
+    assert call([1, 2], n=-1) == moe.MOE_EINVAL
+    assert call([1, 2], H=100) == moe.MOE_EINVAL
+    assert call([1, 2], src_=None) == moe.MOE_EINVAL
+    assert call([1, 10]) == moe.MOE_EINVAL  # row outside the source bank
+    assert "rows[1]" in moe.moe_last_error()
+    assert call([-1]) == moe.MOE_EINVAL
+    assert call([0, 1, 2, 3, 4]) == moe.MOE_EINVAL  # 5 rows into a 4-row stage
+    assert "dst holds" in moe.moe_last_error()
+    assert call([1], dst_=moe.MoeBankC(p, p, p, p, 4, 1)) == moe.MOE_EINVAL  # dst on the host
+    assert L.moe_stage_rows_dma(ctypes.byref(src), None, 1, ctypes.byref(dst), 256, 128, 3,
+                                None) == moe.MOE_EINVAL  # rows NULL
+    assert call([]) == moe.MOE_OK  # nothing to copy
+
+
 def test_finalize_and_counts_reject_bad_args(L):
     p = 0x1000
     assert L.moe_finalize(p, p, 4, 2, 12, p, None) == moe.MOE_EINVAL

@@ -136,3 +136,35 @@ def test_staged_full_shape_decode_bitwise():
         Y0, o0, _ = _run(hb, cb, rm, ids, w, x, H, I, None, **{side: torch.cuda.Stream()})
         Y1, o1, _ = _run(hb, cb, rm, ids, w, x, H, I, stage, **{side: torch.cuda.Stream()})
         assert np.array_equal(Y0, Y1) and np.array_equal(o0, o1)
+
+
+def test_dma_stage_equals_kernel_stage_and_in_place():
+    """moe_stage_rows_dma (the DMA engines, from the active rows read back to
+    the host) copies the same bytes as moe_stage_rows, and the layer run
+    through it gives the bits of the in-place run; a second call with fewer
+    cold picks reuses the stage."""
+    E, k, H, I = 32, 4, 1024, 512
+    rm, ho, co = synth.random_map(E, 10, 7)
+    hot = device_bank(host_bank(ho, 7, 0, H, I))
+    cold_arr = host_bank(co, 7, 0, H, I)
+    cold = pinned_bank(cold_arr)
+    for T, seed in ((24, 0), (5, 1)):
+        ids, w = synth.skewed_routing(T, k, E, 7, 0, seed)
+        x = synth.activations(T, H, 7 + seed)
+        log(f"dma stage: T={T}")
+        Y0, out0, _ = _run(hot, cold, rm, ids, w, x, H, I, None)
+        stage = ColdStage(min(10, T * k), H, I, dma=True)
+        Y1, out1, bufs = _run(hot, cold, rm, ids, w, x, H, I, stage)
+        assert np.array_equal(Y1, Y0) and np.array_equal(out1, out0)
+        active, _, _ = bufs.cold_split.to_host()
+        n = len(active)
+        assert n == int(stage.n_host[0])
+        for name in ("w13", "s13", "w2", "s2"):
+            got = getattr(stage.bank, name)[:n].cpu().numpy()
+            assert np.array_equal(got, cold_arr[name][active]), name
+        # the kernel copy of the same rows gives the same stage bytes
+        kstage = ColdStage(min(10, T * k), H, I)
+        moe.moe_stage_rows(cold, bufs.cold_split, T, k, kstage.bank, kstage.rows, H, I)
+        torch.cuda.synchronize()
+        for name in ("w13", "s13", "w2", "s2"):
+            assert torch.equal(getattr(kstage.bank, name)[:n], getattr(stage.bank, name)[:n])
