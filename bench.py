@@ -87,6 +87,11 @@ def parse():
                          "~40 GB/s in place; the copy runs at the link's ~55 GB/s). dma: "
                          "the staging copy by the DMA engines (moe_stage_rows_dma) from the "
                          "active rows read back to the host after the split")
+    ap.add_argument("--cold-scales", default="host", choices=["host", "device"],
+                    help="host: the cold bank whole in pinned host memory (the pages' layout); "
+                         "device: its E8M0 scale tensors (1/16 of the weight bytes) in HBM, so "
+                         "only the E2M1 weights cross the host link (moe_bank on_host = "
+                         "MOE_BANK_HOST_WEIGHTS)")
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "step40", "highconc", "offdomain",
                              "domainshift", "refit", "counter", "swap"],
@@ -269,6 +274,7 @@ def main():
     Lr, seed = args.layers, args.seed
     sz = synth.expert_sizes(H, I)
     b13, b2 = sz["w13"] + sz["s13"], sz["w2"] + sz["s2"]
+    link_b, cold_hbm_b = cold_bytes_split(sz, args.cold_scales)
     log = lambda m: print(m, file=sys.stderr, flush=True)
 
     ceilings = {} if args.no_ceilings else measure_ceilings(torch)
@@ -286,7 +292,7 @@ def main():
                         for s in synth.tensor_shapes(n_cold, H, I).values()], on_host=True)
         synth.fill_bank_host(cb.tensors(), co, seed, l, H, I)
         hot.append(hb)
-        cold.append(cb)
+        cold.append(place_cold_scales(moe, cb, args.cold_scales))
         maps_host.append(rm.copy())
         maps_dev.append(torch.from_numpy(rm.copy()).cuda())
         hot_owner.append(ho.copy())
@@ -395,7 +401,8 @@ def main():
         cold_act = T * H * 2 + pc * I * 4 + pc * H * 2          # x read, h write+read, Y write
         fin = T * k * H * 2 + T * k * 4 + T * H * 2
         split = T * k * 4 + E * 4 + (T * k * 4) * 2
-        return gu, gu + dn + cold_act + fin + split, uc * (b13 + b2), uh, uc, pc
+        return (gu, gu + dn + cold_act + fin + split + uc * cold_hbm_b, uc * link_b, uh, uc,
+                pc)
 
     # Everything the timed loop records or waits on is created beforehand, so
     # the host work per step is the library calls themselves (the step must
@@ -734,7 +741,8 @@ def main():
                                "domain shift A-B-A" if shift else "in-domain"),
                    "routing": ("verify windows of 7" if routing == "window" else "independent"),
                    "intermediate": I, "tokens": T, "hot_rows": n_hot, "cold_rows": n_cold,
-                   "weights": "mxfp4", "cold_bank": COLD_BANK[args.cold_path], "map": args.map,
+                   "weights": "mxfp4", "cold_bank": COLD_BANK[args.cold_path],
+                   "cold_scales": args.cold_scales, "map": args.map,
                    "layer_banks_rotated": Lr, "cold_stream": not args.serial,
                    "streams": "serial" if args.serial else args.streams,
                    "graph": bool(args.graph), "policy": not args.no_policy,
@@ -830,7 +838,22 @@ def sources_sha256(rel_paths):
     return h.hexdigest() if rel_paths else None
 
 
-def make_layer_banks(torch, moe, synth, E, n_cold, H, I, Lr, seed, map_kind="fitted"):
+def place_cold_scales(moe, cb, scales):
+    """The filled cold bank (all pinned) as it is, or with its scale tensors
+    moved to HBM and only the weights left on the host."""
+    if scales == "host":
+        return cb
+    return moe.Bank(cb.w13, cb.s13.cuda(), cb.w2, cb.s2.cuda(), on_host=moe.BANK_HOST_WEIGHTS)
+
+
+def cold_bytes_split(sz, scales):
+    """(bytes of one cold expert that cross the host link, bytes it reads from HBM)."""
+    w, sc = sz["w13"] + sz["w2"], sz["s13"] + sz["s2"]
+    return (w + sc, 0) if scales == "host" else (w, sc)
+
+
+def make_layer_banks(torch, moe, synth, E, n_cold, H, I, Lr, seed, map_kind="fitted",
+                     cold_scales="host"):
     """Per layer: hot bank (HBM, device-filled), cold bank (pinned host), maps."""
     n_hot = E - n_cold
     hot, cold, maps_host = [], [], []
@@ -844,7 +867,7 @@ def make_layer_banks(torch, moe, synth, E, n_cold, H, I, Lr, seed, map_kind="fit
                         for s in synth.tensor_shapes(n_cold, H, I).values()], on_host=True)
         synth.fill_bank_host(cb.tensors(), co, seed, l, H, I)
         hot.append(hb)
-        cold.append(cb)
+        cold.append(place_cold_scales(moe, cb, cold_scales))
         maps_host.append(rm.copy())
     return hot, cold, maps_host
 
@@ -1007,7 +1030,9 @@ def run_prefill(args):
     b13, b2 = sz["w13"] + sz["s13"], sz["w2"] + sz["s2"]
     log = lambda m: print(m, file=sys.stderr, flush=True)
     steps, warmup = min(args.steps, 16), min(args.warmup, 2)
-    hot, cold, maps_host = make_layer_banks(torch, moe, synth, E, n_cold, H, I, Lr, seed, args.map)
+    hot, cold, maps_host = make_layer_banks(torch, moe, synth, E, n_cold, H, I, Lr, seed, args.map,
+                                            args.cold_scales)
+    link_b, _ = cold_bytes_split(sz, args.cold_scales)
     maps_dev = [torch.from_numpy(m.copy()).cuda() for m in maps_host]
     S = warmup + steps
     ids_np = np.empty((S, T, k), np.int32)
@@ -1103,6 +1128,7 @@ def run_prefill(args):
         "config": {"workload": f"full_layer_prefill_t{T}", "experts": E, "top_k": k,
                    "hidden": H, "intermediate": I, "tokens": T, "hot_rows": n_hot,
                    "cold_rows": n_cold, "weights": "mxfp4", "cold_bank": COLD_BANK[args.cold_path],
+                   "cold_scales": args.cold_scales,
                    "map": args.map, "layer_banks_rotated": Lr, "counter": False,
                    "cold_stream": not args.serial},
         "us_per_layer": round(ms * 1e3, 1),
@@ -1121,7 +1147,7 @@ def run_prefill(args):
                      "down_TFLOPs": round(tf_dn, 1)},
         "hot_hbm": {"achieved": round(hbm_hot, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(hbm_hot / PEAK_HBM_GBPS, 4)},
-        "cold_link_GBps": round(float((uc * (b13 + b2)).sum() / cf.sum() / 1e9), 1),
+        "cold_link_GBps": round(float((uc * link_b).sum() / cf.sum() / 1e9), 1),
         "routing": {"hot_unique_per_step": round(float(uh.mean()), 2),
                     "cold_unique_per_step": round(float(uc.mean()), 2),
                     "cold_share_of_picks": round(float(pc.sum() / (ph + pc).sum()), 4)},

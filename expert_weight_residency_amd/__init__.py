@@ -189,16 +189,22 @@ def moe_ffn_workspace_bytes(T: int, k: int, H: int, I: int) -> int:
 
 # ------------------------------------------------------------ containers --
 
+# where a bank's tensors sit (moe_bank.on_host)
+BANK_DEVICE, BANK_HOST, BANK_HOST_WEIGHTS = 0, 1, 2
+
+
 @dataclass
 class Bank:
     """One residency bank: uint8 tensors w13 [R,2I,H/2], s13 [R,2I,H/32],
-    w2 [R,H,I/2], s2 [R,H,I/32] on the device, or pinned on the host
-    (on_host=True, read in place by the kernels)."""
+    w2 [R,H,I/2], s2 [R,H,I/32] on the device (on_host=False / BANK_DEVICE),
+    all four pinned on the host (on_host=True / BANK_HOST, read in place by
+    the kernels), or w13, w2 pinned on the host and the scales s13, s2 on the
+    device (BANK_HOST_WEIGHTS)."""
     w13: object
     s13: object
     w2: object
     s2: object
-    on_host: bool = False
+    on_host: int = BANK_DEVICE
 
     @property
     def n_rows(self) -> int:
@@ -210,15 +216,20 @@ class Bank:
                self.s2.data_ptr(), self.n_rows, self.on_host)
         c = self.__dict__.get("_abi")
         if c is None or c[0] != key:
+            where = int(self.on_host)
+            if where not in (BANK_DEVICE, BANK_HOST, BANK_HOST_WEIGHTS):
+                raise MoeError(MOE_EINVAL, f"bank on_host={self.on_host!r}: expected "
+                               "BANK_DEVICE, BANK_HOST or BANK_HOST_WEIGHTS")
             for name, t in self.tensors().items():
                 if str(t.dtype) != "torch.uint8" or not t.is_contiguous():
                     raise _bad(f"bank {name}", "a contiguous uint8 tensor", t)
-                if self.on_host and (t.device.type != "cpu" or not t.is_pinned()):
-                    raise _bad(f"bank {name}", "pinned host memory (on_host=True)", t)
-                if not self.on_host and t.device.type != "cuda":
-                    raise _bad(f"bank {name}", "GPU memory (on_host=False)", t)
+                host = where == BANK_HOST or (where == BANK_HOST_WEIGHTS and name[0] == "w")
+                if host and (t.device.type != "cpu" or not t.is_pinned()):
+                    raise _bad(f"bank {name}", f"pinned host memory (on_host={where})", t)
+                if not host and t.device.type != "cuda":
+                    raise _bad(f"bank {name}", f"GPU memory (on_host={where})", t)
             c = (key, MoeBankC(self.w13.data_ptr(), self.s13.data_ptr(), self.w2.data_ptr(),
-                               self.s2.data_ptr(), self.n_rows, 1 if self.on_host else 0))
+                               self.s2.data_ptr(), self.n_rows, where))
             self.__dict__["_abi"] = c
         return c[1]
 

@@ -56,14 +56,21 @@ int check_split(const moe_split& s, const char* name) {
 // Device-visible addresses of a bank's tensors (pinned host memory is
 // translated with hipHostGetDevicePointer).
 int bank_device_ptrs(const moe_bank* b, const uint8_t* out[4]) {
+  if (b->on_host != MOE_BANK_DEVICE && b->on_host != MOE_BANK_HOST &&
+      b->on_host != MOE_BANK_HOST_WEIGHTS)
+    return fail(MOE_EINVAL, "bank on_host=%d is not MOE_BANK_DEVICE, _HOST or _HOST_WEIGHTS",
+                b->on_host);
   void* src[4] = {b->w13, b->s13, b->w2, b->s2};
   for (int i = 0; i < 4; ++i) {
     if (!src[i]) return fail(MOE_EINVAL, "bank tensor %d is NULL", i);
-    if (b->on_host) {
+    // tensors 0 and 2 are the weights, 1 and 3 the scales
+    const bool host = b->on_host == MOE_BANK_HOST || (b->on_host == MOE_BANK_HOST_WEIGHTS && !(i & 1));
+    if (host) {
       void* d = nullptr;
       if (hipHostGetDevicePointer(&d, src[i], 0) != hipSuccess || !d) {
         (void)hipGetLastError();
-        return fail(MOE_EINVAL, "bank tensor %d is not pinned host memory (on_host=1)", i);
+        return fail(MOE_EINVAL, "bank tensor %d is not pinned host memory (on_host=%d)", i,
+                    b->on_host);
       }
       out[i] = static_cast<const uint8_t*>(d);
     } else {
@@ -279,7 +286,7 @@ int moe_stage_rows_dma(const moe_bank* src, const int32_t* rows, int n, const mo
   const bool gu = parts & MOE_STAGE_GATE_UP, dn = parts & MOE_STAGE_DOWN;
   const uint64_t rb[4] = {gu ? (uint64_t)2 * I * (H / 2) : 0, gu ? (uint64_t)2 * I * (H / 32) : 0,
                           dn ? (uint64_t)H * (I / 2) : 0, dn ? (uint64_t)H * (I / 32) : 0};
-  const hipMemcpyKind kind = src->on_host ? hipMemcpyHostToDevice : hipMemcpyDeviceToDevice;
+  const hipMemcpyKind kind = hipMemcpyDefault;  // the tensors of a bank may sit on either side
   hipStream_t st = static_cast<hipStream_t>(stream);
   // one copy per run of consecutive source rows (they land on consecutive
   // destination rows), per tensor

@@ -72,10 +72,17 @@ extern "C" {
 
 /* One residency bank. The four pointers are device-accessible: device memory
  * for the hot bank; for the cold bank, pinned host memory (hipHostMalloc or
- * torch pin_memory) with on_host = 1, which the kernels read in place over the
- * host link ("We Built the Counter", section 1: cold experts sit in host memory
- * and are read in place whenever the router picks one). A cold bank may also
- * live in device memory (on_host = 0); results are identical either way. */
+ * torch pin_memory) with on_host = MOE_BANK_HOST, which the kernels read in
+ * place over the host link ("We Built the Counter", section 1: cold experts
+ * sit in host memory and are read in place whenever the router picks one). A
+ * cold bank may also live in device memory (MOE_BANK_DEVICE), or keep its
+ * weight tensors w13, w2 in pinned host memory and its scale tensors s13, s2
+ * (1/16 of the weight bytes) in device memory (MOE_BANK_HOST_WEIGHTS: only
+ * the weights cross the link); results are identical in every case. Any other
+ * on_host value is refused with MOE_EINVAL. */
+#define MOE_BANK_DEVICE 0
+#define MOE_BANK_HOST 1
+#define MOE_BANK_HOST_WEIGHTS 2
 typedef struct moe_bank {
     void *w13;
     void *s13;

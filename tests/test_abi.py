@@ -136,6 +136,9 @@ def test_stage_rows_dma_rejects_bad_args(L):
     assert call([0, 1, 2, 3, 4]) == moe.MOE_EINVAL  # 5 rows into a 4-row stage
     assert "dst holds" in moe.moe_last_error()
     assert call([1], dst_=moe.MoeBankC(p, p, p, p, 4, 1)) == moe.MOE_EINVAL  # dst on the host
+    assert call([1], dst_=moe.MoeBankC(p, p, p, p, 4, moe.BANK_HOST_WEIGHTS)) == moe.MOE_EINVAL
+    assert call([1], src_=moe.MoeBankC(p, p, p, p, 10, 3)) == moe.MOE_EINVAL  # no such placement
+    assert "on_host=3" in moe.moe_last_error()
     assert L.moe_stage_rows_dma(ctypes.byref(src), None, 1, ctypes.byref(dst), 256, 128, 3,
                                 None) == moe.MOE_EINVAL  # rows NULL
     assert call([]) == moe.MOE_OK  # nothing to copy
@@ -201,6 +204,15 @@ def test_binding_rejects_bad_tensors(L):
     with pytest.raises(moe.MoeError) as e:  # not pinned
         host.abi()
     assert "pinned" in str(e.value)
+    split_host = moe.Bank(*(torch.zeros((2, 4), dtype=torch.uint8) for _ in range(4)),
+                          on_host=moe.BANK_HOST_WEIGHTS)
+    with pytest.raises(moe.MoeError) as e:  # weights must be pinned host memory
+        split_host.abi()
+    assert "bank w13" in str(e.value) and "pinned" in str(e.value)
+    nowhere = moe.Bank(*(torch.zeros((2, 4), dtype=torch.uint8) for _ in range(4)), on_host=3)
+    with pytest.raises(moe.MoeError) as e:
+        nowhere.abi()
+    assert e.value.code == moe.MOE_EINVAL and "on_host=3" in str(e.value)
     wrong = moe.Bank(*(torch.zeros((2, 4), dtype=torch.int16) for _ in range(4)))
     with pytest.raises(moe.MoeError) as e:
         wrong.abi()

@@ -75,3 +75,36 @@ def test_host_bank_equals_device_bank_and_oracle(case):
         ref = oracle.expert_ffn(ob.w13[e], ob.s13[e], ob.w2[e], ob.s2[e], x[t], H, I)["y_bf16"]
         err = rel_errors(Yh[s], ref)
         assert err[0] <= REL_L2 and err[1] <= MAX_REL, (name, s, err)
+
+
+def _split_host_bank(arrays: dict) -> moe.Bank:
+    """Weights pinned on the host, scales in device memory."""
+    w = pinned_bank(arrays)
+    s = device_bank(arrays)
+    return moe.Bank(w.w13, s.s13, w.w2, s.s2, on_host=moe.BANK_HOST_WEIGHTS)
+
+
+SPLIT_CASES = [
+    # name, E, k, H, I, T: host kernels (T <= 16), token-tiled / resident, FP4 (T >= 256)
+    ("h4096_i2880_t16", 10, 6, 4096, 2880, 16),
+    ("h2048_i1472_t7", 8, 4, 2048, 1472, 7),
+    ("h1024_i512_t40", 12, 4, 1024, 512, 40),
+    ("h1024_i512_t300", 12, 4, 1024, 512, 300),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_host_weights_device_scales_bank_equals_host_bank(case):
+    """A bank whose weights sit in pinned host memory and whose scales sit in
+    HBM gives the same bits as the all-host and all-device banks."""
+    name, E, k, H, I, T = case
+    print(f"host-weights bank case {name}: E={E} k={k} H={H} I={I} T={T}", flush=True)
+    seed = 91
+    arrays = host_bank(np.arange(E, dtype=np.int32), seed, 0, H, I)
+    ids, _ = synth.skewed_routing(T, k, E, seed, 0, 0)
+    x = synth.activations(T, H, seed)
+    Yd = _ffn(device_bank(arrays), ids, x, E, k, H, I)
+    Yh = _ffn(pinned_bank(arrays), ids, x, E, k, H, I)
+    Ys = _ffn(_split_host_bank(arrays), ids, x, E, k, H, I)
+    assert np.array_equal(Ys, Yh), name
+    assert np.array_equal(Ys, Yd), name

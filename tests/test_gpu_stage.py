@@ -168,3 +168,27 @@ def test_dma_stage_equals_kernel_stage_and_in_place():
         torch.cuda.synchronize()
         for name in ("w13", "s13", "w2", "s2"):
             assert torch.equal(getattr(kstage.bank, name)[:n], getattr(stage.bank, name)[:n])
+
+
+def test_host_weights_bank_in_place_and_staged():
+    """A cold bank with its weights pinned on the host and its scales in HBM
+    gives, in place, staged by the kernel and staged by the DMA engines, the
+    bits of the all-host cold bank in place."""
+    E, k, H, I = 32, 4, 1024, 512
+    rm, ho, co = synth.random_map(E, 10, 9)
+    hot = device_bank(host_bank(ho, 9, 0, H, I))
+    cold_arr = host_bank(co, 9, 0, H, I)
+    cold = pinned_bank(cold_arr)
+    w, s = pinned_bank(cold_arr), device_bank(cold_arr)
+    split_cold = moe.Bank(w.w13, s.s13, w.w2, s.s2, on_host=moe.BANK_HOST_WEIGHTS)
+    for T, seed in ((16, 0), (40, 1)):
+        ids, wt = synth.skewed_routing(T, k, E, 9, 0, seed)
+        x = synth.activations(T, H, 9 + seed)
+        log(f"host-weights cold bank: T={T}")
+        Y0, out0, _ = _run(hot, cold, rm, ids, wt, x, H, I, None)
+        Y1, out1, _ = _run(hot, split_cold, rm, ids, wt, x, H, I, None)
+        assert np.array_equal(Y1, Y0) and np.array_equal(out1, out0)
+        for dma in (False, True):
+            stage = ColdStage(min(10, T * k), H, I, dma=dma)
+            Y2, out2, _ = _run(hot, split_cold, rm, ids, wt, x, H, I, stage)
+            assert np.array_equal(Y2, Y0) and np.array_equal(out2, out0), dma

@@ -18,11 +18,17 @@ pytestmark = pytest.mark.gpu
 E, N_COLD, K, H, I, SEED = 384, 89, 6, 256, 128, 77
 
 
-def _setup(cold_pinned=True):
+def _setup(cold_at="pinned"):
     rm, ho, co = synth.fitted_map(E, N_COLD, SEED, 0)
     hot_h, cold_h = host_bank(ho, SEED, 0, H, I), host_bank(co, SEED, 0, H, I)
     hot = device_bank(hot_h)
-    cold = pinned_bank(cold_h) if cold_pinned else device_bank(cold_h)
+    if cold_at == "pinned":
+        cold = pinned_bank(cold_h)
+    elif cold_at == "device":
+        cold = device_bank(cold_h)
+    else:  # weights pinned on the host, scales in HBM
+        w, s = pinned_bank(cold_h), device_bank(cold_h)
+        cold = moe.Bank(w.w13, s.s13, w.w2, s.s2, on_host=moe.BANK_HOST_WEIGHTS)
     ob_hot, ob_cold = oracle.Bank(**{k: v.copy() for k, v in hot_h.items()}), \
         oracle.Bank(**{k: v.copy() for k, v in cold_h.items()})
     rm_dev = torch.from_numpy(rm.copy()).cuda()
@@ -39,9 +45,10 @@ def _layer(hot, cold, rm_np, ids, w, x):
     return run_layer(hot, cold, rm_np, ids, w, x, H, I)[1]
 
 
-@pytest.mark.parametrize("cold_pinned", [True, False], ids=["cold_pinned", "cold_device"])
-def test_five_ordered_swaps(cold_pinned):
-    rm, ho, co, hot, cold, ob_hot, ob_cold, rm_dev, staging = _setup(cold_pinned)
+@pytest.mark.parametrize("cold_at", ["pinned", "device", "host_weights"],
+                         ids=["cold_pinned", "cold_device", "cold_host_weights"])
+def test_five_ordered_swaps(cold_at):
+    rm, ho, co, hot, cold, ob_hot, ob_cold, rm_dev, staging = _setup(cold_at)
     rng = np.random.default_rng(1)
     pairs = [(int(rng.integers(len(ho))), int(rng.integers(len(co)))) for _ in range(5)]
     ids, w = synth.skewed_routing(16, K, E, SEED, 0, 0)
