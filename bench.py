@@ -23,8 +23,13 @@ bandwidth of the whole step (algorithmic HBM bytes per step / wall time per
 step); `us_per_layer` is the same step time in microseconds. `roofline` covers
 the hot-bank gate/up kernel (the kernel that moves the most HBM bytes) and
 `roofline_hot_bank` the hot bank's two GEMM kernels together, both timed with
-HIP events on the hot bank's stream in every timed step (that stream is off
-the step's critical path whenever the step has a cold pick). Events on the
+HIP events on the hot bank's stream (that stream is off the step's critical
+path whenever the step has a cold pick): an event before gate/up and one after
+down in every timed step, and on every KERNEL_SPLIT_EVERY-th timed step one
+between the two kernels as well. That middle marker holds the down launch back
+by ~14 us (kernel traces: 0 us between the two kernels without it), so the
+pair's time comes from the steps without it and each kernel's own time from
+the steps with it. Events on the
 main stream (step and cold-path times) would each add ~5 us to the step, so
 they are taken in a separate untimed pass over the first timed steps
 (--profile-steps); the step time itself is the wall clock over all timed
@@ -56,6 +61,7 @@ PEAK_HBM_GBPS = 8000.0
 COLD_BANK = {"inplace": "pinned_host_in_place", "staged": "pinned_host_staged_to_hbm",
              "dma": "pinned_host_dma_copied_to_hbm"}
 NOMINAL_LINK_GBPS = 63.0
+KERNEL_SPLIT_EVERY = 8  # timed steps with an event between hot gate/up and down
 
 
 def parse():
@@ -385,7 +391,7 @@ def main():
     swaps = stale = 0
 
     # hot-stream events of the timed steps, and every event of the profile pass
-    ev = {name: [] for name in ("gu0", "gu1", "dn1")}
+    ev = {name: [] for name in ("gu0", "gu1", "dn1")}  # gu1: every KERNEL_SPLIT_EVERY-th step
     pev = {name: [] for name in ("gu0", "gu1", "dn1", "c0", "c1", "s0", "s1")}
     bytes_step, hot_bytes_gu, cold_bytes, uh_list, uc_list, cold_picks = [], [], [], [], [], 0
     uh_first = []  # distinct hot experts of each step's first layer call (the timed one)
@@ -462,7 +468,7 @@ def main():
             mark("gu0", hot_s)
         moe.moe_expert_gate_up_mxfp4(hot[l], bufs.hot_split, xc, k, I, bufs.workspace,
                                      stream=hot_s)
-        if timed:
+        if timed and (in_profile or (c // lps - base) % KERNEL_SPLIT_EVERY == 0):
             mark("gu1", hot_s)
         moe.moe_expert_down_mxfp4(hot[l], bufs.hot_split, T, k, H, I, bufs.workspace, bufs.Y,
                                   stream=hot_s)
@@ -671,7 +677,16 @@ def main():
     K = args.steps
     ms_per_step = (t1 - t0) * 1e3 / K
     ms = lambda e, a, b: np.array([x.elapsed_time(y) for x, y in zip(e[a], e[b])])
-    gu_ms, dn_ms = ms(ev, "gu0", "gu1"), ms(ev, "gu1", "dn1")       # every timed step
+    # the timed steps with a marker between the two hot kernels (split) and without
+    split = np.arange(len(ev["gu0"])) % KERNEL_SPLIT_EVERY == 0
+    ev_split = {"gu0": [e for e, f in zip(ev["gu0"], split) if f], "gu1": ev["gu1"],
+                "dn1": [e for e, f in zip(ev["dn1"], split) if f]}
+    ev_pair = {"gu0": [e for e, f in zip(ev["gu0"], split) if not f],
+               "dn1": [e for e, f in zip(ev["dn1"], split) if not f]}
+    if not ev_pair["gu0"]:  # too few steps: the pair from the split steps
+        ev_pair = ev_split
+    gu_ms, dn_ms = ms(ev_split, "gu0", "gu1"), ms(ev_split, "gu1", "dn1")
+    pair_ms = ms(ev_pair, "gu0", "dn1")
     pgu_ms, pdn_ms = ms(pev, "gu0", "gu1"), ms(pev, "gu1", "dn1")   # profile pass
     c_ms, st_ms = ms(pev, "c0", "c1"), ms(pev, "s0", "s1")
 
@@ -697,12 +712,15 @@ def main():
                        np.array_equal(maps_dev[l].cpu().numpy(), maps_host[l]) for l in range(Lr))}
     # per-kernel events exist only for eager steps (not inside a replayed graph)
     kern = len(gu_ms) > 0
-    hot_bytes_gu_a = np.asarray(hot_bytes_gu, np.float64)
-    has_cold = np.asarray(cold_bytes, np.float64) > 0
+    pair_steps = ~split if (~split).any() else split
+    hot_bytes_gu_a = np.asarray(hot_bytes_gu, np.float64)[split] if kern else None
+    has_cold = np.asarray(cold_bytes, np.float64)[split] > 0 if kern else None
+    pair_cold = np.asarray(cold_bytes, np.float64)[pair_steps] > 0 if kern else None
     mean_us = lambda v: round(float(v.mean() * 1e3), 1) if len(v) else None
     achieved = float(hot_bytes_gu_a.sum() / (gu_ms.sum() / 1e3) / 1e9) if kern else None
-    hot_ffn_bytes = np.asarray(uh_first, np.float64) * (b13 + b2)
-    achieved_hot = (float(hot_ffn_bytes.sum() / ((gu_ms.sum() + dn_ms.sum()) / 1e3) / 1e9)
+    hot_ffn_bytes = (np.asarray(uh_first, np.float64)[pair_steps] * (b13 + b2) if kern
+                     else None)
+    achieved_hot = (float(hot_ffn_bytes.sum() / (pair_ms.sum() / 1e3) / 1e9)
                     if kern else None)
     value = float(np.mean(bytes_step) / (ms_per_step / 1e3) / 1e9)
     # cold bytes of the profile pass's steps (the same calls, on the maps at its time)
@@ -761,6 +779,11 @@ def main():
         "hot_gate_up_us_by_step": ({"without_cold": mean_us(gu_ms[~has_cold]),
                                     "with_cold": mean_us(gu_ms[has_cold])} if kern else None),
         "hot_down_us": mean_us(dn_ms),
+        "hot_gate_up_down_us": mean_us(pair_ms) if kern else None,
+        "hot_gate_up_down_us_by_step": ({"without_cold": mean_us(pair_ms[~pair_cold]),
+                                         "with_cold": mean_us(pair_ms[pair_cold])}
+                                        if kern else None),
+        "kernel_split_steps": int(split.sum()) if kern else 0,
         "cold_ffn_us": mean_us(c_ms),
         "hot_ffn_GBps": round(achieved_hot, 1) if kern else None,
         "kernels": {"hot_gate_up": fam_gu, "hot_down": fam_dn},
@@ -781,6 +804,8 @@ def main():
         "percentiles_us": {name: pct(v) for name, v in (("step_profile_pass", st_ms),
                                                         ("hot_gate_up", gu_ms),
                                                         ("hot_down", dn_ms),
+                                                        ("hot_gate_up_down",
+                                                         pair_ms if kern else []),
                                                         ("cold_path_profile_pass", c_ms))},
         # host time to enqueue one step (no waiting): it must stay below the
         # step's device time for the step to measure the device
@@ -793,7 +818,8 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBPS, 4) if kern else None,
                      "traffic": traffic if fam_gu == TRAFFIC_KERNEL else None},
         # the hot bank as a whole: gate/up + down algorithmic bytes (each
-        # touched expert's 18.8 MB once) over the two kernels' event times
+        # touched expert's 18.8 MB once) over the span from before gate/up to
+        # after down, in the timed steps without a marker between the two
         "roofline_hot_bank": {"kernels": f"{fam_gu} + {fam_dn}", "bound": "hbm",
                               "achieved": round(achieved_hot, 1) if kern else None,
                               "peak": PEAK_HBM_GBPS, "unit": "GB/s",
