@@ -848,8 +848,10 @@ def ffn_families(T, k, H, I, cap):
     tiled = T * k >= 2 * cap
     gu = ("ffn_gate_up_resident" if T <= 16 and H % 1024 == 0 else
           "ffn_tiled" if tiled else "ffn_gate_up")
+    n, wrb = -(-I // 256), I // 2
+    aligned = n % 4 == 0 and max(r * wrb % 128 for r in range(8)) + wrb - 128 * (n - 1) <= 128
     dn = ("ffn_tiled" if tiled else
-          "ffn_down_resident" if -(-I // 256) % 6 == 0 else "ffn_down")
+          "ffn_down_resident" if I % 32 == 0 and (n % 3 == 0 or aligned) else "ffn_down")
     return gu, dn
 
 

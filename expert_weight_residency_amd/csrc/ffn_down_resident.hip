@@ -22,12 +22,14 @@
 //    chunks) behind one barrier; if they do not fit, it runs phases of as many
 //    rows as fit, and an item's weights are streamed once per phase holding
 //    some of its slots.
-//  - Each wavefront then streams its items' weight chunks back to back, kP
+//  - Each wavefront then streams its items' weight chunks back to back, a few
 //    ahead in a register ring, across item boundaries; only weight loads and
 //    one scale-block load per item go through the vector-memory queue. Each
 //    chunk of a 16-row item is read as two whole-line loads (rows 0-7, rows
 //    8-15) and the halves are exchanged between partner lanes (see
-//    mxfp4_common.h).
+//    mxfp4_common.h). For a bank in HBM whose rows allow it, every load reads
+//    one aligned 128-byte line with the streaming cache policy, and each
+//    chunk is put together on chip from two of them (see kAligned below).
 //  - An item's scale bytes (16 * kNG rows x I/32 bytes) are contiguous and
 //    16-byte aligned: the wavefront loads them with a few 16-byte loads when
 //    its prefetch enters the item, copies them into its own LDS slot when it
@@ -43,6 +45,8 @@
 //  - Each output element sees the same MFMA sequence as in the other kernel
 //    families (same 256-element chunks, same lane-to-element map, same order
 //    from zero) and the same rounding, so a pick gives the same bits.
+#include <algorithm>
+
 #include "internal.h"
 #include "mxfp4_common.h"
 
@@ -51,17 +55,22 @@ namespace {
 
 using namespace mx;
 
-// 8 wavefronts with 2 chunks each in flight: a sweep of the decode step at
-// H = 4096, I = 2880 (hot bank alone, us per launch; wavefronts x chunks):
-// 16x5 92.8, 16x2 90.1, 12x5 91.5, 12x2 89.6, 10x2 89.3, 8x5 88.4, 8x3 87.4,
-// 8x2 86.2, 8x1 86.3, 6x3 86.0, 6x2 85.6, 4x5 94.8, 4x11 96.6, 8x11 91.8.
-// More requests in flight than the CU needs to keep its share of HBM busy
-// only evict, between the two chunks that read it, the line a 1440-byte row
-// shares with its neighbour (with the streaming cache policy 16x5 takes 104.9).
+// 8 wavefronts. Unaligned loads, 2 chunks each in flight: a sweep of the
+// decode step at H = 4096, I = 2880 (hot bank alone, us per launch;
+// wavefronts x chunks): 16x5 92.8, 16x2 90.1, 12x5 91.5, 12x2 89.6, 10x2 89.3,
+// 8x5 88.4, 8x3 87.4, 8x2 86.2, 8x1 86.3, 6x3 86.0, 6x2 85.6, 4x5 94.8, 4x11
+// 96.6, 8x11 91.8: more requests in flight than the CU needs to keep its
+// share of HBM busy only evict, between the two chunks that read it, the line
+// a 1440-byte row shares with its neighbour (with the streaming cache policy
+// 16x5 takes 104.9). Aligned streaming loads (each line read once), 3 chunks
+// in flight, in an A/B against the unaligned kernel's 83.6: 8x3 78.3-78.7,
+// 12x3 78.2, 16x3 78.3, 16x2 77.9, 8x2 83.2, 8x5 78.8, 8x11 83.0, 6x3 88.9;
+// aligned with the ordinary cache policy, 8x2: 85.0.
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kNG = 1;    // 16-row MFMA groups per item
 constexpr int kP = 2;     // weight chunks in flight per wavefront (ring of kP + 1)
+constexpr int kPAl = 3;   // the same with line-aligned loads
 constexpr int kSbl = 2;   // 16-byte scale granules per lane per item (covers I <= 4096 / kNG)
 constexpr size_t kLdsMax = 160 * 1024;  // gfx950: the LDS of one CU
 
@@ -84,6 +93,25 @@ __host__ __device__ inline size_t lds_bytes(const Shape& s, int max_rows) {
   return (size_t)max_rows * s.kpad * 2 + (size_t)kWaves * s.sbw + (size_t)max_rows * 4;
 }
 
+// kAligned: every weight load reads whole aligned lines. Rows of I/2 bytes
+// start m = (row * I/2) mod 128 bytes into a line (0, 32, 64 or 96 at
+// I = 2880), so the operand layout's chunk c of a row (128 bytes from the row
+// start) straddles two lines, and a line is read once by each of the two
+// chunks that share it (twice the line requests, and the line at a row
+// boundary is read again a row later). Instead load c of a row reads the
+// row's c-th aligned line (from the row start rounded down), and chunk c is
+// put together on chip from loads c and c + 1: lane piece p (16 bytes) takes
+// piece p + m/16 of the two lines' concatenation. The source lane of that
+// piece sends load c's value if the piece lies in the first line, else load
+// c + 1's, and one ds_bpermute per dword moves it; the lanes then hold exactly
+// the bytes the unaligned loads would give (same MFMA inputs, same bits). The
+// last chunk needs only load c when m + (its bytes) <= 128 for every row,
+// which the launcher checks (an item's 16 rows are line-aligned as a whole
+// when the tensor is, so its last row's last line ends at the item's end and
+// its first row's first line starts at the item's start: no load leaves the
+// item). Each line is read by one load, so the loads take the streaming cache
+// policy (78 against 84 us per decode step with the unaligned loads).
+template <bool kAligned>
 __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
     const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
     const int32_t* __restrict__ n_active, const int32_t* __restrict__ active_rows,
@@ -200,21 +228,55 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
     // zero, accumulated from +0).
     const bool upper = r >= 8;
     const bool lane_in_last = (nchunk - 1) * kChunkBlocks + 2 * q < nblk;
-    const size_t off_a = line_load_a(r, q, wrb), off_b = line_load_b(r, q, wrb);
-    const size_t last_a = (nchunk - 1) * 128 + (lane_in_last ? off_a : off_a - 32 * q);
-    const size_t last_b = (nchunk - 1) * 128 + (lane_in_last ? off_b : off_b - 32 * q);
-    // Ordinary cache policy here: rows of I/2 bytes are not line-aligned, so
-    // a line holding the end of one chunk and the start of the next is read
-    // by two loads a chunk apart, and with the streaming policy it is gone by
-    // the second (measured: whole-line loads 115 -> 102 us per decode step
-    // with the ordinary policy, no gain with the streaming one). The
-    // scheduling barrier pins the loads at their place in the stream (left
-    // free, the compiler sinks them towards the end of a ring cycle, which
-    // shortens how far ahead they run).
+    // kAligned: rows 8 + r and r start equally far into a line (8 rows are
+    // 8 * I/2 bytes, a multiple of 128)
+    const uint32_t mis = kAligned ? (uint32_t)(((size_t)(r & 7) * wrb) & 127u) : 0u;
+    const size_t off_a = line_load_a(r, q, wrb) - mis, off_b = line_load_b(r, q, wrb) - mis;
+    const size_t last_a =
+        (nchunk - 1) * 128 + (kAligned || lane_in_last ? off_a : off_a - 32 * q);
+    const size_t last_b =
+        (nchunk - 1) * 128 + (kAligned || lane_in_last ? off_b : off_b - 32 * q);
+    // kAligned: this lane's 16-byte piece of its row in loads A and B, the
+    // shift in pieces, whether the piece it holds is passed on from load c
+    // (else from load c + 1), and the lane holding the piece it needs
+    const int shift = (int)(mis >> 4);
+    const int pa_me = 2 * q + (r >= 8 ? 1 : 0), pb_me = 2 * q + (r < 8 ? 1 : 0);
+    const bool send_first_a = pa_me >= shift, send_first_b = pb_me >= shift;
+    const int pa_src = (pa_me + shift) & 7, pb_src = (pb_me + shift) & 7;
+    const int addr_a = ((r & 7) + 8 * (pa_src & 1) + 16 * (pa_src >> 1)) * 4;
+    const int addr_b = ((r & 7) + 8 * (1 - (pb_src & 1)) + 16 * (pb_src >> 1)) * 4;
+    auto realign = [&](const AChunk& first, const AChunk& second) {
+      AChunk o;
+      auto mv = [&](uint32_t x, uint32_t y, bool f, int addr) {
+        return (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)(f ? x : y));
+      };
+      o.lo.x = mv(first.lo.x, second.lo.x, send_first_a, addr_a);
+      o.lo.y = mv(first.lo.y, second.lo.y, send_first_a, addr_a);
+      o.lo.z = mv(first.lo.z, second.lo.z, send_first_a, addr_a);
+      o.lo.w = mv(first.lo.w, second.lo.w, send_first_a, addr_a);
+      o.hi.x = mv(first.hi.x, second.hi.x, send_first_b, addr_b);
+      o.hi.y = mv(first.hi.y, second.hi.y, send_first_b, addr_b);
+      o.hi.z = mv(first.hi.z, second.hi.z, send_first_b, addr_b);
+      o.hi.w = mv(first.hi.w, second.hi.w, send_first_b, addr_b);
+      return o;
+    };
+    // Unaligned loads take the ordinary cache policy: rows of I/2 bytes are
+    // not line-aligned, so a line holding the end of one chunk and the start
+    // of the next is read by two loads a chunk apart, and with the streaming
+    // policy it is gone by the second (measured: whole-line loads 115 -> 102
+    // us per decode step with the ordinary policy, no gain with the streaming
+    // one). The scheduling barrier pins the loads at their place in the
+    // stream (left free, the compiler sinks them towards the end of a ring
+    // cycle, which shortens how far ahead they run).
     auto load_w = [&](AChunk& a) {
       const bool last = p_c == nchunk - 1;
-      a.lo = *reinterpret_cast<const uint4*>(pw + (last ? last_a : p_c * 128 + off_a));
-      a.hi = *reinterpret_cast<const uint4*>(pw + (last ? last_b : p_c * 128 + off_b));
+      if constexpr (kAligned) {
+        a.lo = ld_stream16(pw + (last ? last_a : p_c * 128 + off_a));
+        a.hi = ld_stream16(pw + (last ? last_b : p_c * 128 + off_b));
+      } else {
+        a.lo = *reinterpret_cast<const uint4*>(pw + (last ? last_a : p_c * 128 + off_a));
+        a.hi = *reinterpret_cast<const uint4*>(pw + (last ? last_b : p_c * 128 + off_b));
+      }
       __builtin_amdgcn_sched_barrier(0);
     };
     // The scale block of the cursor's item, kSbl granules per lane (separate
@@ -230,12 +292,13 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    AChunk ring[kP + 1];
+    constexpr int P = kAligned ? kPAl : kP;
+    AChunk ring[P + 1];
     load_sblk();
 #pragma unroll
-    for (int p = 0; p < kP; ++p) {
+    for (int p = 0; p < P; ++p) {
       load_w(ring[p]);
-      ++p_c;  // kP < nchunk
+      ++p_c;  // P < nchunk
     }
 
     // The items the cursor took, and their passes, in order; nchunk is a
@@ -264,12 +327,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
         // One loop body for every ring cycle (a separate copy for the last
         // cycle would keep the ring in other registers, and moving them
         // between copies waits for every load in flight).
-        for (int c = 0; c < nchunk; c += kP + 1) {
+        for (int c = 0; c < nchunk; c += P + 1) {
 #pragma unroll
-          for (int u = 0; u <= kP; ++u) {
+          for (int u = 0; u <= P; ++u) {
             const int cc = c + u;
-            load_w(ring[(u + kP) % (kP + 1)]);
-            if (u == 0 && c + kP + 1 == nchunk) {
+            load_w(ring[(u + P) % (P + 1)]);
+            if (u == 0 && c + P + 1 == nchunk) {
               p_rollover();
               load_sblk();
             } else {
@@ -281,12 +344,17 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
             const uint32_t b = ok ? raw : 0x7f7fu;
             const float s0 = e8m0_to_f32(b & 0xffu), s1 = e8m0_to_f32(b >> 8);
             const int e0 = cc * kChunkElems + 64 * q;
+            AChunk wc;
+            if constexpr (kAligned)
+              wc = realign(ring[u], ring[(u + 1) % (P + 1)]);
+            else
+              wc = ring[u];
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
               const bf16x8 bv =
                   *reinterpret_cast<const bf16x8*>(hs + lds_elem(lrow, kpad, e0 + 8 * m));
               acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  dequant8(own_word(ring[u], m, upper), m < 4 ? s0 : s1), bv, acc, 0, 0, 0);
+                  dequant8(own_word(wc, m, upper), m < 4 ? s0 : s1), bv, acc, 0, 0, 0);
             }
           }
         }
@@ -321,9 +389,27 @@ int rows_that_fit(const Shape& s, int want) {
 
 }  // namespace
 
-bool ffn_use_down_resident(int T, int k, int H, int I, const void* s2) {
+namespace {
+// Line-aligned loads (device banks): the weight tensor 128-byte aligned, so
+// that every item starts on a line, and the last chunk's bytes of every row
+// inside the row's last aligned line, m + (I/2 - 128 (nchunk - 1)) <= 128 for
+// each row's offset m into its first line; whole ring turns per pass.
+bool down_aligned(int I, const void* w2, int on_host) {
   const Shape s = shape_of(I);
-  return T >= 1 && I % 32 == 0 && H % (16 * kNG) == 0 && s.nchunk % (kP + 1) == 0 &&
+  const int wrb = I / 2, last = wrb - 128 * (s.nchunk - 1);
+  int mmax = 0;
+  for (int r = 0; r < 8; ++r) mmax = std::max(mmax, (r * wrb) & 127);
+  return !on_host && (reinterpret_cast<uintptr_t>(w2) & 127u) == 0 && mmax + last <= 128 &&
+         s.nchunk % (kPAl + 1) == 0;
+}
+}  // namespace
+
+bool ffn_use_down_resident(int T, int k, int H, int I, const void* w2, const void* s2,
+                           int on_host) {
+  const Shape s = shape_of(I);
+  return T >= 1 && I % 32 == 0 && H % (16 * kNG) == 0 &&
+         (s.nchunk % (kP + 1) == 0 || down_aligned(I, w2, on_host)) &&
+         (reinterpret_cast<uintptr_t>(w2) & 15u) == 0 &&
          s.sbw % 16 == 0 && s.sbw <= kSbl * 64 * 16 &&
          (reinterpret_cast<uintptr_t>(s2) & 15u) == 0 && rows_that_fit(s, T * k) >= 1;
 }
@@ -336,8 +422,9 @@ hipError_t launch_down_resident(const uint8_t* w2, const uint8_t* s2, int cap, i
   const int max_rows = rows_that_fit(s, T * k);
   const int cus = device_cus();
   const int grid = on_host ? kHostBankCUs : (cus > 2 * kHostBankCUs ? cus - kHostBankCUs : cus);
-  hipLaunchKernelGGL(ffn_down_resident, dim3(grid), dim3(kThreads), lds_bytes(s, max_rows),
-                     stream, w2, s2, sp.n_active, sp.active_rows, sp.row_off, sp.slots,
+  auto kern = down_aligned(I, w2, on_host) ? ffn_down_resident<true> : ffn_down_resident<false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds_bytes(s, max_rows), stream, w2, s2,
+                     sp.n_active, sp.active_rows, sp.row_off, sp.slots,
                      reinterpret_cast<const __bf16*>(h_ws), H, I, max_rows, Y);
   return hipGetLastError();
 }

@@ -298,7 +298,7 @@ hipError_t launch_down(const uint8_t* w2, const uint8_t* s2, int cap, int on_hos
     return launch_down_host(w2, s2, sp, T, k, H, I, h_ws, Y, stream);
   if (ffn_use_tiled(T, k, cap))
     return launch_down_tiled(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
-  if (ffn_use_down_resident(T, k, H, I, s2))
+  if (ffn_use_down_resident(T, k, H, I, w2, s2, on_host))
     return launch_down_resident(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
   const int w = on_host ? kWavesHost : kWavesDevice;
   const int blocks = (H / (16 * kNG) + w - 1) / w;

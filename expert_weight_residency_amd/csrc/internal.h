@@ -65,8 +65,11 @@ hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int c
 
 // Down GEMM as a persistent streaming kernel with the workgroup's h rows in
 // LDS (ffn_down_resident.hip): I a multiple of 32 whose chunk count is a
-// multiple of the ring length, a 16-byte aligned scale tensor; either bank.
-bool ffn_use_down_resident(int T, int k, int H, int I, const void* s2);
+// multiple of the ring length (of the unaligned or, for a device bank with a
+// 128-byte aligned weight tensor, the line-aligned loads), 16-byte aligned
+// weight and scale tensors; either bank.
+bool ffn_use_down_resident(int T, int k, int H, int I, const void* w2, const void* s2,
+                           int on_host);
 hipError_t launch_down_resident(const uint8_t* w2, const uint8_t* s2, int cap, int on_host,
                                 const moe_split& split, int T, int k, int H, int I,
                                 const uint16_t* h_ws, uint16_t* Y, hipStream_t stream);

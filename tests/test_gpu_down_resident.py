@@ -15,6 +15,11 @@ instead when the same scale bytes sit 2 bytes off 16-byte alignment:
     phases);
   - the bank in pinned host memory (8 workgroups) against the same bank in HBM
     (all CUs but 8): the work split differs, the bits must not.
+For a bank in HBM with a 128-byte aligned weight tensor, shapes whose rows
+allow it (I = 2880, 2048, 1856 here) take line-aligned loads, each chunk put
+together on chip from two lines; with the weight tensor 16 bytes off a line
+the same bank takes the unaligned loads (I = 2880) or the decode down kernel
+(I = 1856, whose 8 chunks are no multiple of the unaligned ring): same bits.
 """
 import numpy as np
 import pytest
@@ -52,6 +57,18 @@ def offset_s2_bank(arrays: dict, off: int = 2) -> moe.Bank:
     return moe.Bank(t["w13"], t["s13"], t["w2"], view, on_host=False)
 
 
+def offset_w2_bank(arrays: dict, off: int = 16) -> moe.Bank:
+    """The bank in HBM with its down-weight tensor starting `off` bytes past a
+    128-byte boundary (same bytes): no line-aligned loads for it."""
+    t = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda() for k, v in arrays.items()}
+    w2 = np.ascontiguousarray(arrays["w2"])
+    buf = torch.zeros(w2.size + 128, dtype=torch.uint8, device="cuda")
+    view = buf[off:off + w2.size].view(w2.shape)
+    view.copy_(torch.from_numpy(w2))
+    assert view.data_ptr() % 128 == off
+    return moe.Bank(t["w13"], t["s13"], view, t["s2"], on_host=False)
+
+
 def _all_hot(E, seed, H, I):
     rm, owners, _ = synth.all_hot_map(E)
     return rm, host_bank(owners, seed, 0, H, I)
@@ -73,8 +90,10 @@ def _vs_oracle(rm, arrays, ids, w, x, H, I, Y):
 
 # banks large enough that every step stays below 2 picks per row (the token-tiled range)
 @pytest.mark.parametrize("shape", [(48, 4, 1024, 1472, 16), (24, 4, 1024, 1536, 9),
-                                   (64, 6, 4096, 2880, 16), (48, 6, 4096, 2880, 3)],
-                         ids=["I1472_T16", "I1536_T9", "I2880_T16", "I2880_T3"])
+                                   (64, 6, 4096, 2880, 16), (48, 6, 4096, 2880, 3),
+                                   (48, 4, 1024, 2048, 16), (48, 4, 1024, 1856, 11)],
+                         ids=["I1472_T16", "I1536_T9", "I2880_T16", "I2880_T3", "I2048_T16",
+                              "I1856_T11"])
 def test_down_resident_matches_oracle(shape):
     E, k, H, I, T = shape
     log(f"down resident vs oracle {shape}")
@@ -139,3 +158,19 @@ def test_down_resident_host_bank_equals_device_bank():
     empty = device_bank(host_bank(np.zeros(0, np.int32), 29, 0, H, I))
     Yh, _, _ = run_layer(empty, pinned_bank(arrays), -1 - rm, ids, w, x, H, I)
     assert np.array_equal(Yd, Yh)
+
+
+@pytest.mark.parametrize("shape", [(64, 6, 4096, 2880, 16), (48, 4, 1024, 1856, 11),
+                                   (40, 4, 1024, 2048, 7)],
+                         ids=["I2880_T16", "I1856_T11", "I2048_T7"])
+def test_down_aligned_loads_equal_unaligned(shape):
+    """Line-aligned loads (weight tensor on a 128-byte boundary) give the bits
+    of the same bank with its weight tensor 16 bytes off a line."""
+    E, k, H, I, T = shape
+    log(f"down aligned == unaligned weight tensor {shape}")
+    rm, arrays = _all_hot(E, 31, H, I)
+    ids, w = synth.skewed_routing(T, k, E, 31, 0, 0)
+    x = synth.activations(T, H, 31)
+    Ya, outa, _ = run_layer(device_bank(arrays), None, rm, ids, w, x, H, I)
+    Yu, outu, _ = run_layer(offset_w2_bank(arrays), None, rm, ids, w, x, H, I)
+    assert np.array_equal(Ya, Yu) and np.array_equal(outa, outu)
