@@ -4,11 +4,9 @@
 // the routed MXFP4 expert FFN per bank), organised so that a wavefront's
 // weight stream never drains:
 //
-//  - One workgroup of 16 wavefronts per CU for a device bank, on all CUs but
-//    the few a host-bank launch beside it holds; for a bank in host memory, 8
-//    wavefronts per workgroup on those few (still enough reads in flight to
-//    fill the link), with the registers to hold each row's whole scale line.
-//    It stages every token row of x
+//  - One workgroup of 8 wavefronts per CU: for a device bank on all CUs but
+//    the few a host-bank launch beside it holds, for a bank in host memory on
+//    those few. It stages every token row of x
 //    (T <= 16 rows of H) and the split's bookkeeping (active rows, offsets,
 //    the token of every slot) into LDS once, behind one barrier; each
 //    wavefront issues its first item's weight loads before that, so the
@@ -30,11 +28,18 @@
 //    exchanged between partner lanes (see mxfp4_common.h): 163 -> 148 us
 //    alone per decode step against the two half-line loads of the operand
 //    layout (the gate/up rows of H/2 = 2048 bytes are line-aligned).
-//  - Scale bytes are loaded once per 4 chunks per row group (8 bytes per
-//    lane, one chunk's scales each) and redistributed across the lane
-//    quarters with two lane-swap instructions: a per-chunk 2-byte load per
-//    lane costs a whole memory instruction for 1/16 of the bytes, and those
-//    instructions, not the bytes, bounded this kernel.
+//  - Each row's scale bytes (one 128-byte line at H = 4096) are loaded once
+//    per item, 32 bytes per lane (the row's four lanes hold the whole line),
+//    and every 4 chunks each lane's pairs are taken from the line with
+//    ds_bpermute and redistributed across the lane quarters with two
+//    lane-swap instructions. A per-chunk 2-byte load per lane cost a whole
+//    memory instruction for 1/16 of the bytes (those instructions, not the
+//    bytes, bounded the first version: 197 -> 164 us per decode step with 8
+//    bytes per lane per 4 chunks); reading the line in four such pieces, ~9
+//    us apart, let the L2 drop it in between (1.07x the algorithmic bytes).
+//    Holding the whole line takes the registers of 8 wavefronts per CU rather
+//    than 16: 142.3 -> 137.5 us per decode step (16 wavefronts with quarter
+//    lines against 8 with whole lines; 12 with whole lines 138.6).
 //  - An item's tokens are the MFMA columns (16 per pass; an expert with more
 //    than 16 slots, which needs duplicate ids in a token, takes more passes).
 //  - Each output element sees the same MFMA sequence as in the other kernel
@@ -48,7 +53,7 @@ namespace {
 
 using namespace mx;
 
-constexpr int kWaves = 16;               // wavefronts per workgroup (one workgroup per CU)
+constexpr int kWaves = 8;                // wavefronts per workgroup (one workgroup per CU)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kNG = 2;                   // MFMA row groups per item (gate, up)
 
@@ -101,18 +106,12 @@ __device__ __forceinline__ uint2 quad_from_line(const uint4 (&blk)[2], int r, in
   return make_uint2(x, y);
 }
 
-// kLine (banks in host memory): 8 wavefronts per workgroup with twice the
-// registers each, and each row's scale bytes read as one 128-byte line per
-// item (2 loads of 16 bytes per lane) instead of a 32-byte piece per row
-// every 4 chunks: over the host link a read of a few bytes per row costs
-// nearly what a whole line does.
-template <int P, bool kLine>
-__global__ __launch_bounds__(kLine ? 512 : kThreads, kLine ? 2 : 4) void ffn_gate_up_resident(
+template <int P>
+__global__ __launch_bounds__(kThreads, 2) void ffn_gate_up_resident(
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
     const int32_t* __restrict__ n_active, const int32_t* __restrict__ active_rows,
     const int32_t* __restrict__ row_off, const int32_t* __restrict__ slots,
     const __bf16* __restrict__ x, int T, int k, int H, int I, uint16_t* __restrict__ h_ws) {
-  constexpr int kT = kLine ? 512 : kThreads;
   extern __shared__ __align__(16) unsigned char smem[];
   const int kpad = (H + kChunkElems - 1) / kChunkElems * kChunkElems;
   __bf16* xs = reinterpret_cast<__bf16*>(smem);
@@ -205,31 +204,32 @@ __global__ __launch_bounds__(kLine ? 512 : kThreads, kLine ? 2 : 4) void ffn_gat
   };
 
   // Weight chunks run P ahead in a ring of P + 1 = 4 (only lo/hi of AChunk are
-  // used). Scale bytes come in quads: at the start of every 4 chunks each
-  // lane loads the 8 scale bytes of one of the next 4 chunks of its row, and
-  // scale_quad turns them into this lane's own pairs, so a wavefront issues
-  // one scale load per row group per 4 chunks instead of one per chunk.
+  // used). Scale bytes come in quads of chunks: at the start of every 4
+  // chunks each lane takes the 8 scale bytes of one of the 4 chunks of its
+  // row from the row's line (quad_from_line), and scale_quad turns them into
+  // this lane's own pairs.
   static_assert(P == 3, "the ring cycle must match the 4-chunk scale quad");
   AChunk ring[P + 1][kNG];
   uint2 sraw[kNG];
-  // kLine: the scale lines of the consumer's item (cur) and of the item the
-  // prefetch cursor entered last (nxt); the consumer's next quad and whether
-  // it starts a new item or pass (then cur takes nxt)
+  // A row's scale bytes are H/32 bytes: one 32-byte piece per quad, four
+  // pieces per 128-byte line. The scale lines of the consumer's item (cur)
+  // and of the line the prefetch cursor entered last (nxt); the consumer's
+  // next quad and whether it starts a new line (then cur takes nxt).
+  const int nq = nchunk >> 2;  // quads per row
+  // Lane quarter q's piece of line L of its row; past the row's last quad a
+  // lane reads piece 0 of the line instead (in bounds; never used).
+  auto sline_off = [&](int L) {
+    return 128 * L + 32 * (4 * L + q < nq ? q : 0);
+  };
   uint4 sb_cur[kNG][2], sb_nxt[kNG][2];
   int s_quad = 0;
   bool s_new = false;
-  if constexpr (kLine) {
 #pragma unroll
-    for (int g = 0; g < kNG; ++g) {
-      sb_cur[g][0] = *reinterpret_cast<const uint4*>(ps[g] + 32 * q);
-      sb_cur[g][1] = *reinterpret_cast<const uint4*>(ps[g] + 32 * q + 16);
-      sb_nxt[g][0] = sb_cur[g][0];
-      sb_nxt[g][1] = sb_cur[g][1];
-    }
-  } else {
-#pragma unroll
-    for (int g = 0; g < kNG; ++g)
-      sraw[g] = *reinterpret_cast<const uint2*>(ps[g] + 8 * (p_c + q));
+  for (int g = 0; g < kNG; ++g) {
+    sb_cur[g][0] = *reinterpret_cast<const uint4*>(ps[g] + sline_off(0));
+    sb_cur[g][1] = *reinterpret_cast<const uint4*>(ps[g] + sline_off(0) + 16);
+    sb_nxt[g][0] = sb_cur[g][0];
+    sb_nxt[g][1] = sb_cur[g][1];
   }
 #pragma unroll
   for (int p = 0; p < P; ++p) {
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kLine ? 512 : kThreads, kLine ? 2 : 4) void ffn_gat
     // entries); nothing reads them. na >= 1 here (the run is not empty).
     constexpr int kB = 8;  // granules of x per thread per batch
     const int gpr = kpad / 8, ng = T * gpr;
-    for (int i0 = 0; i0 <= na || i0 < picks; i0 += kT) {
+    for (int i0 = 0; i0 <= na || i0 < picks; i0 += kThreads) {
       const int i = i0 + tid;
       const int ir = i < na ? i : na - 1, io = i <= na ? i : na, is = i < picks ? i : picks - 1;
       const int vr = active_rows[ir], vo = row_off[io], vs = slots[is];
@@ -257,13 +257,13 @@ __global__ __launch_bounds__(kLine ? 512 : kThreads, kLine ? 2 : 4) void ffn_gat
       l_slot[is] = vs;
       l_tok[is] = vs / k;
     }
-    for (int b0 = 0; b0 < ng; b0 += kB * kT) {
+    for (int b0 = 0; b0 < ng; b0 += kB * kThreads) {
       uint4 v[kB];
       int dst[kB];
       uint32_t pad = 0;  // bit u: granule u is zero padding past H
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
-        const int gi = min(b0 + u * kT + tid, ng - 1);
+        const int gi = min(b0 + u * kThreads + tid, ng - 1);
         const int n = gi / gpr, g = gi - n * gpr;
         v[u] = *reinterpret_cast<const uint4*>(x + (size_t)n * H + (g * 8 < H ? g * 8 : 0));
         pad |= (g * 8 >= H ? 1u : 0u) << u;
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kLine ? 512 : kThreads, kLine ? 2 : 4) void ffn_gat
       for (int u = 0; u < kB; ++u)
         *reinterpret_cast<uint4*>(xs + dst[u]) = (pad >> u) & 1u ? make_uint4(0, 0, 0, 0) : v[u];
     }
-    if (tid == 0) l_next = g0 + kT / 64;  // waves start on items g0 + wave
+    if (tid == 0) l_next = g0 + kThreads / 64;  // waves start on items g0 + wave
   }
   __syncthreads();
 
@@ -295,17 +295,15 @@ __global__ __launch_bounds__(kLine ? 512 : kThreads, kLine ? 2 : 4) void ffn_gat
       f32x4 acc[kNG] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       for (int c = 0; c < nchunk; c += P + 1) {
         uint32_t sx[kNG], sy[kNG];
-        if constexpr (kLine) {
-          if (s_new) {
+        if (s_new) {
 #pragma unroll
-            for (int g = 0; g < kNG; ++g) {
-              sb_cur[g][0] = sb_nxt[g][0];
-              sb_cur[g][1] = sb_nxt[g][1];
-            }
+          for (int g = 0; g < kNG; ++g) {
+            sb_cur[g][0] = sb_nxt[g][0];
+            sb_cur[g][1] = sb_nxt[g][1];
           }
-#pragma unroll
-          for (int g = 0; g < kNG; ++g) sraw[g] = quad_from_line(sb_cur[g], r, q, s_quad);
         }
+#pragma unroll
+        for (int g = 0; g < kNG; ++g) sraw[g] = quad_from_line(sb_cur[g], r, q, s_quad & 3);
 #pragma unroll
         for (int g = 0; g < kNG; ++g) scale_quad(sraw[g], sx[g], sy[g]);
 #pragma unroll
@@ -316,20 +314,15 @@ __global__ __launch_bounds__(kLine ? 512 : kThreads, kLine ? 2 : 4) void ffn_gat
           p_advance();
           if (u == 0) {
             // the cursor now stands at the first chunk of the next quad
-            if constexpr (kLine) {
-              s_quad = p_c >> 2;
-              s_new = p_c == 0;
-              if (p_c == 0) {  // a new item or pass: its rows' scale lines
+            s_quad = p_c >> 2;
+            s_new = (p_c & 15) == 0;
+            if (s_new) {  // a new item, pass or line: the rows' next scale line
+              const int off = sline_off(p_c >> 4);
 #pragma unroll
-                for (int g = 0; g < kNG; ++g) {
-                  sb_nxt[g][0] = *reinterpret_cast<const uint4*>(ps[g] + 32 * q);
-                  sb_nxt[g][1] = *reinterpret_cast<const uint4*>(ps[g] + 32 * q + 16);
-                }
+              for (int g = 0; g < kNG; ++g) {
+                sb_nxt[g][0] = *reinterpret_cast<const uint4*>(ps[g] + off);
+                sb_nxt[g][1] = *reinterpret_cast<const uint4*>(ps[g] + off + 16);
               }
-            } else {
-#pragma unroll
-              for (int g = 0; g < kNG; ++g)
-                sraw[g] = *reinterpret_cast<const uint2*>(ps[g] + 8 * (p_c + q));
             }
           }
           float sc[kNG][2];
@@ -366,11 +359,11 @@ __global__ __launch_bounds__(kLine ? 512 : kThreads, kLine ? 2 : 4) void ffn_gat
   }
 }
 
-template <int P, bool kLine>
+template <int P>
 hipError_t launch_p(const uint8_t* w13, const uint8_t* s13, int cap, const moe_split& sp,
                     const uint16_t* x, int T, int k, int H, int I, uint16_t* h_ws,
                     hipStream_t stream, int cus) {
-  hipLaunchKernelGGL((ffn_gate_up_resident<P, kLine>), dim3(cus), dim3(kLine ? 512 : kThreads),
+  hipLaunchKernelGGL((ffn_gate_up_resident<P>), dim3(cus), dim3(kThreads),
                      resident_lds_bytes(T, k, H, cap), stream, w13, s13, sp.n_active,
                      sp.active_rows, sp.row_off, sp.slots, reinterpret_cast<const __bf16*>(x), T,
                      k, H, I, h_ws);
@@ -380,10 +373,10 @@ hipError_t launch_p(const uint8_t* w13, const uint8_t* s13, int cap, const moe_s
 }  // namespace
 
 bool ffn_use_resident(int T, int k, int H, int cap, const void* s13) {
-  // H a multiple of 1024: whole 4-chunk quads per row, 8-byte scale loads
-  // inside the row; the scale tensor 8-byte aligned for those loads.
+  // H a multiple of 1024: whole 4-chunk quads per row, 16-byte scale loads
+  // inside the row; the scale tensor 16-byte aligned for those loads.
   return T >= 1 && T <= 16 && H % 1024 == 0 &&
-         (reinterpret_cast<uintptr_t>(s13) & 7u) == 0 &&
+         (reinterpret_cast<uintptr_t>(s13) & 15u) == 0 &&
          resident_lds_bytes(T, k, H, cap) <= kResidentMaxLds;
 }
 
@@ -391,12 +384,12 @@ hipError_t launch_gate_up_resident(const uint8_t* w13, const uint8_t* s13, int c
                                    const moe_split& sp, const uint16_t* x, int T, int k, int H,
                                    int I, uint16_t* h_ws, hipStream_t stream) {
   const int cus = device_cus();
-  // A bank in host memory runs on kHostBankCUs workgroups (16 wavefronts,
-  // 3 chunks each in flight: enough to fill the host link); a device bank on
-  // the other CUs.
-  if (on_host) return launch_p<3, true>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, kHostBankCUs);
+  // A bank in host memory runs on kHostBankCUs workgroups (3 chunks in
+  // flight per wavefront: enough to fill the host link); a device bank on the
+  // other CUs.
+  if (on_host) return launch_p<3>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, kHostBankCUs);
   const int grid = cus > 2 * kHostBankCUs ? cus - kHostBankCUs : cus;
-  return launch_p<3, false>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, grid);
+  return launch_p<3>(w13, s13, cap, sp, x, T, k, H, I, h_ws, stream, grid);
 }
 
 }  // namespace moe

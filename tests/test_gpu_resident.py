@@ -4,7 +4,9 @@ The library runs it for device-resident banks when 1 <= T <= 16 (decode). It
 must match the oracle within tolerance (relative L2 <= 1e-2, max relative <=
 3e-2, every slot on its own) and give the same bits as the other kernel
 families for every pick:
-  - decode shapes (T = 1, 7, 16 at full H = 4096, I = 2880; a ragged I);
+  - decode shapes (T = 1, 7, 16 at full H = 4096, I = 2880; a ragged I; a row
+    whose scale bytes fill a quarter line (H = 1024), three quarters (3072)
+    or two lines (8192));
   - an expert picked by all 16 tokens (one full 16-token pass) and an expert
     with 64 slots from duplicate ids (four passes);
   - bitwise against the decode kernel (steps with T > 16), with the bank in
@@ -53,8 +55,9 @@ def _check(rm, hot, cold, ids, w, x, H, I, cold_pinned=False):
 
 
 @pytest.mark.parametrize("shape", [(48, 6, 4096, 2880, 1), (48, 6, 4096, 2880, 7),
-                                   (48, 6, 4096, 2880, 16), (24, 4, 1024, 320, 16)],
-                         ids=["T1", "T7", "T16", "I320_T16"])
+                                   (48, 6, 4096, 2880, 16), (24, 4, 1024, 320, 16),
+                                   (24, 4, 3072, 512, 16), (16, 4, 8192, 512, 8)],
+                         ids=["T1", "T7", "T16", "I320_T16", "H3072_T16", "H8192_T8"])
 def test_resident_matches_oracle(shape):
     E, k, H, I, T = shape
     log(f"resident {shape}")
@@ -104,9 +107,13 @@ def test_resident_equals_decode_kernel_bitwise(where):
     assert np.array_equal(Y20[: 4 * k], Y4)
 
 
-def test_resident_host_bank_matches_oracle():
-    """Resident kernel reading a bank in pinned host memory, against the oracle."""
-    E, k, H, I, T = 32, 6, 4096, 2880, 16
+@pytest.mark.parametrize("shape", [(32, 6, 4096, 2880, 16), (16, 4, 8192, 512, 8)],
+                         ids=["H4096_T16", "H8192_T8"])
+def test_resident_host_bank_matches_oracle(shape):
+    """Resident kernel reading a bank in pinned host memory, against the oracle
+    (at H = 8192, above the host-bank kernels' limit, the cold bank's gate/up
+    runs the resident kernel on the host bank's few CUs)."""
+    E, k, H, I, T = shape
     rm, ho, co = synth.random_map(E, 8, 17)
     hot, cold = host_bank(ho, 17, 0, H, I), host_bank(co, 17, 0, H, I)
     ids, w = synth.skewed_routing(T, k, E, 17, 0, 0)
