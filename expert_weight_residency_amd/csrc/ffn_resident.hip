@@ -19,10 +19,11 @@
 //    one after another and leave the last part of the launch with few loads
 //    in flight). Each wavefront streams its items' weight chunks back to
 //    back, kP chunks ahead in a register ring, so the prefetch runs straight
-//    across item boundaries. Inside the loop the only global loads are the
-//    weight chunks, issued unconditionally (past the wavefront's last chunk
-//    it re-reads its last 4 chunks, still in cache), so waiting for one chunk
-//    never waits for a newer one.
+//    across item boundaries. Inside the loop the global loads are the weight
+//    chunks, issued unconditionally (past the wavefront's last chunk it
+//    re-reads its last 4 chunks, still in cache), so waiting for one chunk
+//    never waits for a newer one, and the scale lines of each item the
+//    prefetch enters.
 //  - Each chunk of a 16-row group is read as two whole-line loads (rows 0-7,
 //    rows 8-15) with the streaming cache policy, and the halves are
 //    exchanged between partner lanes (see mxfp4_common.h): 163 -> 148 us
