@@ -289,6 +289,9 @@ hipError_t launch_gate_up(const uint8_t* w13, const uint8_t* s13, int cap, int o
   return hipGetLastError();
 }
 
+constexpr int kSmallBankRows = 96;        // banks this small prefer the persistent down kernel
+constexpr int kSmallBankPicksPerRow = 8;  // ... below this many picks per row
+
 hipError_t launch_down(const uint8_t* w2, const uint8_t* s2, int cap, int on_host,
                        const moe_split& sp, int T, int k, int H, int I, const uint16_t* h_ws,
                        uint16_t* Y, hipStream_t stream) {
@@ -296,10 +299,20 @@ hipError_t launch_down(const uint8_t* w2, const uint8_t* s2, int cap, int on_hos
     return launch_down_fp4(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
   if (on_host && ffn_use_down_host(T, k, H, I, s2))
     return launch_down_host(w2, s2, sp, T, k, H, I, h_ws, Y, stream);
-  if (ffn_use_tiled(T, k, cap))
+  // A device bank of few rows (the step's staged cold rows) holds few active
+  // experts: the token-tiled kernel then runs one workgroup per 512 weight
+  // rows per 64-token tile and leaves most CUs idle, while the persistent
+  // kernel spreads 16-row items over all of them (89-row stage at T = 32, 64,
+  // 112: 2.1, 1.7, 1.2% less per layer). From kSmallBankPicksPerRow picks per
+  // row the tiled kernel's one weight read per 64 tokens counts for more.
+  const bool small = !on_host && cap <= kSmallBankRows &&
+                     (long long)T * k < (long long)kSmallBankPicksPerRow * cap;
+  if (!small && ffn_use_tiled(T, k, cap))
     return launch_down_tiled(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
   if (ffn_use_down_resident(T, k, H, I, w2, s2, on_host))
     return launch_down_resident(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
+  if (ffn_use_tiled(T, k, cap))
+    return launch_down_tiled(w2, s2, cap, on_host, sp, T, k, H, I, h_ws, Y, stream);
   const int w = on_host ? kWavesHost : kWavesDevice;
   const int blocks = (H / (16 * kNG) + w - 1) / w;
   auto kern = on_host ? ffn_down<kPHost, kWavesHost> : ffn_down<kPDevice, kWavesDevice>;
