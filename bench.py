@@ -29,7 +29,9 @@ down in every timed step, and on every KERNEL_SPLIT_EVERY-th timed step one
 between the two kernels as well. That middle marker holds the down launch back
 by ~14 us (kernel traces: 0 us between the two kernels without it), so the
 pair's time comes from the steps without it and each kernel's own time from
-the steps with it. Events on the
+the steps with it. Neither uses the first timed step when there are others: it
+starts from the idle device that the opening synchronize leaves and runs
+slower (the step time includes it). Events on the
 main stream (step and cold-path times) would each add ~5 us to the step, so
 they are taken in a separate untimed pass over the first timed steps
 (--profile-steps); the step time itself is the wall clock over all timed
@@ -61,7 +63,18 @@ PEAK_HBM_GBPS = 8000.0
 COLD_BANK = {"inplace": "pinned_host_in_place", "staged": "pinned_host_staged_to_hbm",
              "dma": "pinned_host_dma_copied_to_hbm"}
 NOMINAL_LINK_GBPS = 63.0
-KERNEL_SPLIT_EVERY = 8  # timed steps with an event between hot gate/up and down
+KERNEL_SPLIT_EVERY = 4  # timed steps with an event between hot gate/up and down
+
+
+def kernel_split_step(i: int, steps: int) -> bool:
+    """Whether timed step i records an event between the hot gate/up and down
+    kernels: the steps in the middle of each group of KERNEL_SPLIT_EVERY (the
+    first step after the synchronize that opens the timed region runs from an
+    idle device, which a short run would over-weight), or the first step when
+    the run is shorter than that."""
+    if steps <= KERNEL_SPLIT_EVERY // 2:
+        return i == 0
+    return i % KERNEL_SPLIT_EVERY == KERNEL_SPLIT_EVERY // 2
 
 
 def parse():
@@ -391,7 +404,7 @@ def main():
     swaps = stale = 0
 
     # hot-stream events of the timed steps, and every event of the profile pass
-    ev = {name: [] for name in ("gu0", "gu1", "dn1")}  # gu1: every KERNEL_SPLIT_EVERY-th step
+    ev = {name: [] for name in ("gu0", "gu1", "dn1")}  # gu1: the kernel_split_step steps
     pev = {name: [] for name in ("gu0", "gu1", "dn1", "c0", "c1", "s0", "s1")}
     bytes_step, hot_bytes_gu, cold_bytes, uh_list, uc_list, cold_picks = [], [], [], [], [], 0
     uh_first = []  # distinct hot experts of each step's first layer call (the timed one)
@@ -468,7 +481,7 @@ def main():
             mark("gu0", hot_s)
         moe.moe_expert_gate_up_mxfp4(hot[l], bufs.hot_split, xc, k, I, bufs.workspace,
                                      stream=hot_s)
-        if timed and (in_profile or (c // lps - base) % KERNEL_SPLIT_EVERY == 0):
+        if timed and (in_profile or kernel_split_step(c // lps - base, args.steps)):
             mark("gu1", hot_s)
         moe.moe_expert_down_mxfp4(hot[l], bufs.hot_split, T, k, H, I, bufs.workspace, bufs.Y,
                                   stream=hot_s)
@@ -678,11 +691,18 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / K
     ms = lambda e, a, b: np.array([x.elapsed_time(y) for x, y in zip(e[a], e[b])])
     # the timed steps with a marker between the two hot kernels (split) and without
-    split = np.arange(len(ev["gu0"])) % KERNEL_SPLIT_EVERY == 0
+    split = np.array([kernel_split_step(i, args.steps) for i in range(len(ev["gu0"]))], bool)
     ev_split = {"gu0": [e for e, f in zip(ev["gu0"], split) if f], "gu1": ev["gu1"],
                 "dn1": [e for e, f in zip(ev["dn1"], split) if f]}
-    ev_pair = {"gu0": [e for e, f in zip(ev["gu0"], split) if not f],
-               "dn1": [e for e, f in zip(ev["dn1"], split) if not f]}
+    # the pair's steps: the others, less the first timed step when there are
+    # more (it starts from the idle device the synchronize leaves, and alone
+    # moved the pair of a 20-step run from 225.7 to ~230 us; the step time
+    # keeps it)
+    pair = ~split
+    if pair.sum() > 1:
+        pair[0] = False
+    ev_pair = {"gu0": [e for e, f in zip(ev["gu0"], pair) if f],
+               "dn1": [e for e, f in zip(ev["dn1"], pair) if f]}
     if not ev_pair["gu0"]:  # too few steps: the pair from the split steps
         ev_pair = ev_split
     gu_ms, dn_ms = ms(ev_split, "gu0", "gu1"), ms(ev_split, "gu1", "dn1")
@@ -712,7 +732,7 @@ def main():
                        np.array_equal(maps_dev[l].cpu().numpy(), maps_host[l]) for l in range(Lr))}
     # per-kernel events exist only for eager steps (not inside a replayed graph)
     kern = len(gu_ms) > 0
-    pair_steps = ~split if (~split).any() else split
+    pair_steps = pair if pair.any() else split
     hot_bytes_gu_a = np.asarray(hot_bytes_gu, np.float64)[split] if kern else None
     has_cold = np.asarray(cold_bytes, np.float64)[split] > 0 if kern else None
     pair_cold = np.asarray(cold_bytes, np.float64)[pair_steps] > 0 if kern else None
@@ -784,6 +804,7 @@ def main():
                                          "with_cold": mean_us(pair_ms[pair_cold])}
                                         if kern else None),
         "kernel_split_steps": int(split.sum()) if kern else 0,
+        "kernel_pair_steps": int(pair_steps.sum()) if kern else 0,
         "cold_ffn_us": mean_us(c_ms),
         "hot_ffn_GBps": round(achieved_hot, 1) if kern else None,
         "kernels": {"hot_gate_up": fam_gu, "hot_down": fam_dn},
