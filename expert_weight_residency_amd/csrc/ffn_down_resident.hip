@@ -109,8 +109,10 @@ __host__ __device__ inline size_t lds_bytes(const Shape& s, int max_rows) {
 // which the launcher checks (an item's 16 rows are line-aligned as a whole
 // when the tensor is, so its last row's last line ends at the item's end and
 // its first row's first line starts at the item's start: no load leaves the
-// item). Each line is read by one load, so the loads take the streaming cache
-// policy (78 against 84 us per decode step with the unaligned loads).
+// item). Each line is then read by one load (but the line a row ends in and
+// the next row starts in, read by both rows about one item apart), so the
+// loads take the streaming cache policy (78 against 84 us per decode step
+// with the unaligned loads).
 template <bool kAligned>
 __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
     const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
