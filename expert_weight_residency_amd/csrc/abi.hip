@@ -335,6 +335,11 @@ int moe_swap_rows(const moe_bank* hot, const moe_bank* cold, int hot_row, int co
     return fail(MOE_EINVAL, "NULL argument");
   if (H <= 0 || H % 64 || I <= 0 || I % 64) return fail(MOE_EINVAL, "H, I must be multiples of 64");
   if (E < 1 || E > MOE_MAX_EXPERTS) return fail(MOE_EINVAL, "E=%d outside [1, %d]", E, MOE_MAX_EXPERTS);
+  for (const moe_bank* b : {hot, cold})
+    if (b->on_host != MOE_BANK_DEVICE && b->on_host != MOE_BANK_HOST &&
+        b->on_host != MOE_BANK_HOST_WEIGHTS)
+      return fail(MOE_EINVAL, "bank on_host=%d is not MOE_BANK_DEVICE, _HOST or _HOST_WEIGHTS",
+                  b->on_host);
   if (hot_row < 0 || hot_row >= hot->n_rows || cold_row < 0 || cold_row >= cold->n_rows)
     return fail(MOE_EINVAL, "rows (%d, %d) outside banks (%d, %d)", hot_row, cold_row,
                 hot->n_rows, cold->n_rows);

@@ -174,6 +174,11 @@ def test_swap_stale_check_runs_on_host(L):
     assert L.moe_swap_rows(ctypes.byref(hot), ctypes.byref(cold), 3, 0, 5, 1, p, 8,
                            hot_owner.ctypes.data, cold_owner.ctypes.data, p, need, 256, 128,
                            None) == moe.MOE_EINVAL
+    nowhere = moe.MoeBankC(p, p, p, p, 2, 3)  # no such placement
+    assert L.moe_swap_rows(ctypes.byref(hot), ctypes.byref(nowhere), 1, 0, 5, 1, p, 8,
+                           hot_owner.ctypes.data, cold_owner.ctypes.data, p, need, 256, 128,
+                           None) == moe.MOE_EINVAL
+    assert "on_host=3" in moe.moe_last_error()
 
 
 def test_python_errors_raise(L):
