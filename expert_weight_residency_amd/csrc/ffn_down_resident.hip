@@ -204,9 +204,11 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
     // of the next item it takes. nchunk is a multiple of the ring length
     // kP + 1, so this happens at one fixed ring position (first step of a
     // pass's last cycle); everywhere else the cursor only steps to the next
-    // chunk. When no item is left the cursor restarts the current one (p_it
-    // unchanged tells the consumer to stop): the few loads still issued after
-    // that (fewer than nchunk) re-read cached chunks and are never used.
+    // chunk. When no item is left the cursor moves to the bank's first item
+    // (p_it unchanged tells the consumer to stop): the few loads still issued
+    // after that (fewer than nchunk) are never used, and every wavefront's
+    // read the same lines, which stay in the L2 (re-reading the wavefront's
+    // own last item, just streamed past the L2, fetched ~12 MB per launch).
     auto p_rollover = [&]() {
       p_c = 0;
       if (p_pass + 1 < p_np) {  // next 16 slots of the same item: its weights again
@@ -219,6 +221,8 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_down_resident(
         p_it = nx;
         p_np = passes_of(nx);
         p_enter(nx);
+      } else {
+        pw = w2;  // the bank's first item, which every wavefront's last loads share
       }
     };
     // Whole-line loads (line_load_a/_b): lane r's partner r^8 has the same q,

@@ -21,7 +21,8 @@
 //    back, kP chunks ahead in a register ring, so the prefetch runs straight
 //    across item boundaries. Inside the loop the global loads are the weight
 //    chunks, issued unconditionally (past the wavefront's last chunk it
-//    re-reads its last 4 chunks, still in cache), so waiting for one chunk
+//    reads 4 chunks of the bank's first rows, shared by every wavefront and
+//    held in the L2), so waiting for one chunk
 //    never waits for a newer one, and the scale lines of each item the
 //    prefetch enters.
 //  - Each chunk of a 16-row group is read as two whole-line loads (rows 0-7,
@@ -197,9 +198,16 @@ __global__ __launch_bounds__(kThreads, 2) void ffn_gate_up_resident(
         p_npass = passes_of(nx);
       } else {
         // Past the wavefront's last chunk the loads only keep the stream
-        // unconditional: cycle through the last quad, which is still cached
-        // (p_it unchanged tells the consumer to stop).
+        // unconditional: every wavefront cycles through the same quad of the
+        // bank's first rows, which stays in the L2 (p_it unchanged tells the
+        // consumer to stop). Its own last quad, just streamed past the L2,
+        // was fetched again: ~24 MB per decode launch.
         p_c = nchunk - 4;
+#pragma unroll
+        for (int g = 0; g < kNG; ++g) {
+          pa[g] = w13 + line_load_a(r, q, wrb);
+          pb[g] = w13 + line_load_b(r, q, wrb);
+        }
       }
     }
   };
