@@ -47,3 +47,16 @@ def test_no_gpu_no_measurement():
     assert p.returncode != 0
     assert "needs a GPU" in p.stderr
     assert '"metric"' not in p.stdout
+
+
+def test_kernel_split_steps():
+    """The timed steps that carry an event between the two hot kernels: the
+    middle of each group of four, never the first step of a longer run (it
+    starts from an idle device); a run of one or two steps uses its first."""
+    sys.path.insert(0, str(ROOT))
+    import bench
+    pick = lambda n: [i for i in range(n) if bench.kernel_split_step(i, n)]
+    assert pick(20) == [2, 6, 10, 14, 18]
+    assert pick(1024)[:3] == [2, 6, 10] and len(pick(1024)) == 256
+    assert pick(3) == [2]
+    assert pick(2) == [0] and pick(1) == [0]
