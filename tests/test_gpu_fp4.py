@@ -89,9 +89,10 @@ def test_fp4_matches_oracle(case):
 
 
 def test_fp4_tile_sizes():
-    """Experts with 1, 15, 16, 17, 63, 64, 65 and 130 tokens (k = 1, 380 tokens):
-    partial column groups, exact tiles, experts spanning up to three tiles."""
-    counts = [9, 1, 15, 16, 17, 63, 64, 65, 130]
+    """Experts with 1, 15, 16, 17, 63, 64, 65, 127, 128, 129 and 257 tokens
+    (k = 1, 891 tokens): partial column groups, exact tiles, experts spanning
+    up to five tiles."""
+    counts = [9, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 257]
     H, I, seed = 512, 256, 71
     E = len(counts)
     rm, ho, co = synth.map_from_cold_set(E, [0])
