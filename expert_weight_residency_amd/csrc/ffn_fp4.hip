@@ -425,14 +425,15 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void ffn_fp4(
           // (past the last chunk they re-read clamped, in-bounds data), so the
           // compiler counts exactly one chunk of weight loads after each copy;
           // only the arithmetic is skipped past the last chunk.
-          // Chunk cc's weights (loaded one step ago) are waited for here,
-          // before the next copies and loads are issued. Left to the compiler,
-          // the wait lands at the first use of those registers, after the
-          // copy just issued; a global-to-LDS copy makes it wait for every
+          // Chunk cc's weights (loaded kP steps ago) are waited for here,
+          // before the next copies and loads are issued (the kP - 1 chunks
+          // issued after them may stay in flight). Left to the compiler, the
+          // wait lands at the first use of those registers, after the copy
+          // just issued; a global-to-LDS copy makes it wait for every
           // outstanding load there, the next chunk's just issued included,
           // and no weight load would overlap the arithmetic.
           __builtin_amdgcn_sched_barrier(0);
-          __builtin_amdgcn_s_waitcnt(vmcnt_lds_imm(0));
+          __builtin_amdgcn_s_waitcnt(vmcnt_lds_imm((kP - 1) * kLoadsPerChunk));
           __builtin_amdgcn_sched_barrier(0);
           // The buffer filled here was last read in chunk cc - 1, which every
           // wavefront finished before the last barrier.
