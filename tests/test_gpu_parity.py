@@ -260,6 +260,35 @@ def test_split_equals_unsplit_many_tokens():
     assert np.array_equal(Ys, Yu) and np.array_equal(outs, outu)
 
 
+@pytest.mark.parametrize("T", [16, 17, 255, 256])
+def test_family_boundaries(T):
+    """Steps on either side of the kernel-family thresholds, H = 1024, I = 512,
+    24 hot rows in HBM and 8 cold rows in pinned host memory: 16 tokens run the
+    resident kernels, 17 the decode kernels (too few picks per row for the
+    token tiles), 255 the token-tiled bf16 kernels and 256 the FP4 kernels.
+    Each against the oracle (every slot on its own), and split == unsplit
+    bitwise (the family depends on T alone, not on the bank)."""
+    E, k, H, I, seed = 32, 2, 1024, 512, 57
+    log(f"family boundary T={T}")
+    rm, ho, co, hot, cold, ids, w, x = _layer_case(E, k, H, I, T, 8, seed, "skewed")
+    Yr, outr, bad = oracle.moe_layer(oracle_bank(hot), oracle_bank(cold), rm, ids, w, x, H, I)
+    assert bad == 0
+    Ys, outs, ninv = run_layer(device_bank(hot), pinned_bank(cold), rm, ids, w, x, H, I)
+    assert ninv == 0
+    Yr = Yr.reshape(T * k, H)
+    e_y, e_o = rel_errors(Ys, Yr), rel_errors(outs, outr)
+    log(f"  Y rel-L2 {e_y[0]:.2e} max-rel {e_y[1]:.2e}; out rel-L2 {e_o[0]:.2e} max-rel {e_o[1]:.2e}")
+    assert e_y[0] <= REL_L2 and e_y[1] <= MAX_REL
+    assert e_o[0] <= REL_L2 and e_o[1] <= MAX_REL
+    for s in range(T * k):
+        r = rel_errors(Ys[s], Yr[s])
+        assert r[0] <= REL_L2, (s, r)
+    all_map, all_owner, _ = synth.all_hot_map(E)
+    Yu, outu, _ = run_layer(device_bank(host_bank(all_owner, seed, 0, H, I)), None, all_map, ids,
+                            w, x, H, I)
+    assert np.array_equal(Ys, Yu) and np.array_equal(outs, outu)
+
+
 def test_empty_step_writes_nothing():
     E, k, H, I = 16, 2, 256, 128
     rm, ho, co, hot, cold, ids, w, x = _layer_case(E, k, H, I, 4, 4, 3, "gaussian")
