@@ -1,0 +1,66 @@
+"""GPU parity at the longest reduction axes the entry points accept.
+
+H and I may each be up to 32768 elements (the bf16 decode kernels stage one
+token's x row of H elements, 64 KB, in LDS). Here H = 32768 (the gate/up
+reduction at its maximum, down over 128) and I = 32768 (down's reduction at
+its maximum, gate/up over 256), each through the bf16 families (8 tokens) and
+the FP4 family (256 tokens: 128 quantized chunks per row), 3 rows in HBM and 1
+in pinned host memory read in place; every slot against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import expert_weight_residency_amd as moe
+import oracle
+import synth
+from gpu_util import (MAX_REL, REL_L2, device_bank, host_bank, oracle_bank, pinned_bank,
+                      rel_errors, run_layer)
+
+pytestmark = pytest.mark.gpu
+
+MAX_K = 32768
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.lib()
+    yield
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+CASES = [
+    # name, H, I, T, k
+    ("H32768_bf16", MAX_K, 128, 8, 2),
+    ("H32768_fp4", MAX_K, 128, 256, 1),
+    ("I32768_bf16", 256, MAX_K, 8, 2),
+    ("I32768_fp4", 256, MAX_K, 256, 1),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_longest_reduction_matches_oracle(case):
+    name, H, I, T, k = case
+    E, seed = 4, 91
+    log(f"max-size case {name}")
+    rm, ho, co = synth.random_map(E, 1, seed)
+    hot, cold = host_bank(ho, seed, 0, H, I), host_bank(co, seed, 0, H, I)
+    ids, w = synth.gaussian_routing(T, k, E, seed)
+    x = synth.activations(T, H, seed)
+    Yr, outr, bad = oracle.moe_layer(oracle_bank(hot), oracle_bank(cold), rm, ids, w, x, H, I)
+    assert bad == 0
+    Y, out, ninv = run_layer(device_bank(hot), pinned_bank(cold), rm, ids, w, x, H, I)
+    assert ninv == 0
+    Yr = Yr.reshape(T * k, H)
+    e_y, e_o = rel_errors(Y, Yr), rel_errors(out, outr)
+    log(f"  Y rel-L2 {e_y[0]:.2e} max-rel {e_y[1]:.2e}; out rel-L2 {e_o[0]:.2e} max-rel {e_o[1]:.2e}")
+    assert e_y[0] <= REL_L2 and e_y[1] <= MAX_REL
+    assert e_o[0] <= REL_L2 and e_o[1] <= MAX_REL
+    for s in range(T * k):
+        r = rel_errors(Y[s], Yr[s])
+        assert r[0] <= REL_L2, (s, r)
+    assert np.isfinite(oracle.bf16_to_f32(Y)).all()
