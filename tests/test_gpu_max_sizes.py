@@ -64,3 +64,47 @@ def test_longest_reduction_matches_oracle(case):
         r = rel_errors(Y[s], Yr[s])
         assert r[0] <= REL_L2, (s, r)
     assert np.isfinite(oracle.bf16_to_f32(Y)).all()
+
+
+def test_fp4_largest_step_sampled():
+    """The largest step the FP4 path accepts at H = 4096: T*k = 524,286 slots,
+    whose quantized x rows end 16 KB below 4 GB (the kernels address them with
+    32-bit offsets; one more token of 6 picks is refused). 8 experts, top-6,
+    I = 256; sampled tokens, the last one holding the highest slots, against
+    the oracle."""
+    from expert_weight_residency_amd.layer import LayerBuffers, ResidencyLayer
+    from gpu_util import routing_tensors
+    H, I, E, k, seed = 4096, 256, 8, 6, 93
+    T = ((1 << 32) // (16 * 512) - 1) // k          # 87,381 tokens: 524,286 slots
+    assert moe.moe_ffn_workspace_bytes(T, k, H, I) > 0
+    assert moe.moe_ffn_workspace_bytes(T + 1, k, H, I) == 0
+    rm, ho, co = synth.random_map(E, 1, seed)
+    hb, cb = host_bank(ho, seed, 0, H, I), host_bank(co, seed, 0, H, I)
+    ids, w = synth.gaussian_routing(T, k, E, seed)
+    x = synth.activations(T, H, seed)
+    log(f"largest FP4 step: T={T}, {T * k} slots")
+    ids_d, w_d, x_d = routing_tensors(ids, w, x)
+    bufs = LayerBuffers.allocate(T, k, H, I, len(ho), len(co))
+    layer = ResidencyLayer(device_bank(hb), device_bank(cb),
+                           torch.from_numpy(np.ascontiguousarray(rm, np.int32)).cuda(), H, I)
+    layer.forward(x_d, ids_d, w_d, bufs)
+    torch.cuda.synchronize()
+    assert int(bufs.n_invalid.item()) == 0
+    rng = np.random.default_rng(5)
+    tokens = np.unique(np.concatenate([[0, T // 2, T - 2, T - 1], rng.choice(T, 4, replace=False)]))
+    tok_d = torch.from_numpy(tokens).cuda()
+    Y = bufs.Y.view(T, k, H)[tok_d].cpu().numpy().view(np.uint16)
+    out = bufs.out[:T][tok_d].cpu().numpy().view(np.uint16)
+    del bufs, layer
+    torch.cuda.empty_cache()
+    Yr, outr, bad = oracle.moe_layer(oracle_bank(hb), oracle_bank(cb), rm, ids[tokens], w[tokens],
+                                     x[tokens], H, I)
+    assert bad == 0
+    e_y, e_o = rel_errors(Y, Yr.reshape(len(tokens), k, H)), rel_errors(out, outr)
+    log(f"  sampled {len(tokens)} tokens: Y {e_y} out {e_o}")
+    assert e_y[0] <= REL_L2 and e_y[1] <= MAX_REL
+    assert e_o[0] <= REL_L2 and e_o[1] <= MAX_REL
+    for i in range(len(tokens)):
+        for j in range(k):
+            r = rel_errors(Y[i, j], Yr.reshape(len(tokens), k, H)[i, j])
+            assert r[0] <= REL_L2, (tokens[i], j, r)
