@@ -108,3 +108,37 @@ def test_fp4_largest_step_sampled():
         for j in range(k):
             r = rel_errors(Y[i, j], Yr.reshape(len(tokens), k, H)[i, j])
             assert r[0] <= REL_L2, (tokens[i], j, r)
+
+
+@pytest.mark.parametrize("T", [8, 64, 256], ids=["T8_decode", "T64_decode", "T256_fp4"])
+def test_most_experts_rows_and_picks(T):
+    """The count limits at once: 4096 experts (MOE_MAX_EXPERTS), 3072 rows in
+    HBM and 1024 in pinned host memory, one 4096-row bank (MOE_MAX_ROWS) for
+    the unsplit run, top-32 (MOE_MAX_TOPK); H = I = 64 keeps the banks small.
+    Every slot against the oracle, split == unsplit bitwise, and the usage
+    counter against the oracle's (steps of at most 256 tokens count)."""
+    E, k, H, I, seed = 4096, 32, 64, 64, 97
+    log(f"count limits T={T}")
+    rm, ho, co = synth.random_map(E, 1024, seed)
+    hot, cold = host_bank(ho, seed, 0, H, I), host_bank(co, seed, 0, H, I)
+    ids, w = synth.gaussian_routing(T, k, E, seed)
+    x = synth.activations(T, H, seed)
+    Yr, outr, bad = oracle.moe_layer(oracle_bank(hot), oracle_bank(cold), rm, ids, w, x, H, I)
+    assert bad == 0
+    counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+    Ys, outs, ninv = run_layer(device_bank(hot), pinned_bank(cold), rm, ids, w, x, H, I,
+                               counts_layer=counts)
+    assert ninv == 0
+    assert np.array_equal(counts.cpu().numpy(), oracle.usage_count(np.zeros(E, np.int32), ids, E))
+    Yr = Yr.reshape(T * k, H)
+    e_y, e_o = rel_errors(Ys, Yr), rel_errors(outs, outr)
+    log(f"  Y rel-L2 {e_y[0]:.2e} max-rel {e_y[1]:.2e}; out rel-L2 {e_o[0]:.2e} max-rel {e_o[1]:.2e}")
+    assert e_y[0] <= REL_L2 and e_y[1] <= MAX_REL
+    assert e_o[0] <= REL_L2 and e_o[1] <= MAX_REL
+    for s in range(T * k):
+        r = rel_errors(Ys[s], Yr[s])
+        assert r[0] <= REL_L2, (s, r)
+    all_map, all_owner, _ = synth.all_hot_map(E)
+    Yu, outu, _ = run_layer(device_bank(host_bank(all_owner, seed, 0, H, I)), None, all_map, ids,
+                            w, x, H, I)
+    assert np.array_equal(Ys, Yu) and np.array_equal(outs, outu)
