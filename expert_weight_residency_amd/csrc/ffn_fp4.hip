@@ -118,26 +118,36 @@ __device__ __forceinline__ int block_exp(float amax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// |v| <= 448, finite -> E4M3 code, round to nearest even (sign kept for -0).
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t s = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = __builtin_fabsf(v);
-  const int ea = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
-  if (ea < -6)  // below the smallest normal: multiples of 2^-9 (8 is the smallest normal)
-    return s | (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 9));
-  uint32_t q = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - ea));  // 8 .. 16
-  int e = ea;
-  if (q == 16) {
-    q = 8;
-    ++e;
-  }
-  return s | (uint32_t)(e + 7) << 3 | (q - 8);
-}
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const int e = (int)((c >> 3) & 15u), m = (int)(c & 7u);
-  const float mag = e ? __builtin_ldexpf((float)(8 + m), e - 10) : __builtin_ldexpf((float)m, -9);
-  return (c & 0x80u) ? -mag : mag;
+// Four finite values with |v| <= 448 -> their E4M3 codes, value i in byte i,
+// rounded to nearest even with the sign kept for -0: gfx950's conversion at
+// scale 1. (On the device it gave the codes of a software round-to-nearest-
+// even on every E4M3 value, every midpoint between neighbours and the f32
+// values on either side of it, +-0, subnormal codes and 4M random values.)
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, a, b, 1.0f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c, d, 1.0f, true);
+  return __builtin_bit_cast(uint32_t, r);
+}
+// The exact values of the E4M3 codes in bytes 2*Hi and 2*Hi + 1 of c.
+template <bool Hi>
+__device__ __forceinline__ v2f e4m3x2_value(uint32_t c) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c, 1.0f, Hi);
+}
+// The two terms of four values v sharing a block exponent e (|v| 2^-e <= 448):
+// returns the four hi codes and leaves in v what they leave over, exactly
+// (v and the rounded term are close).
+__device__ __forceinline__ uint32_t split_hi(float& v0, float& v1, float& v2, float& v3, int e) {
+  const uint32_t c = e4m3x4(__builtin_ldexpf(v0, -e), __builtin_ldexpf(v1, -e),
+                            __builtin_ldexpf(v2, -e), __builtin_ldexpf(v3, -e));
+  const v2f a = e4m3x2_value<false>(c), b = e4m3x2_value<true>(c);
+  v0 -= __builtin_ldexpf(a.x, e);
+  v1 -= __builtin_ldexpf(a.y, e);
+  v2 -= __builtin_ldexpf(b.x, e);
+  v3 -= __builtin_ldexpf(b.y, e);
+  return c;
 }
 
 // Byte offset, inside a chunk's 256 bytes of one term, of element w (0..31)
@@ -190,18 +200,17 @@ __global__ __launch_bounds__(256) void quant_x_slots(
 #pragma unroll
     for (int w = 0; w < 32; ++w) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[w]));
     const int eh = block_exp(amax);
-    uint32_t hi[8] = {0, 0, 0, 0, 0, 0, 0, 0}, lo[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) hi[d] = split_hi(v[4 * d], v[4 * d + 1], v[4 * d + 2], v[4 * d + 3], eh);
     float ramax = 0.f;
 #pragma unroll
-    for (int w = 0; w < 32; ++w) {
-      const uint32_t ch = e4m3_rne(__builtin_ldexpf(v[w], -eh));
-      hi[w >> 2] |= ch << (8 * (w & 3));
-      v[w] -= __builtin_ldexpf(e4m3_value(ch), eh);  // exact: v and the rounded term are close
-      ramax = __builtin_fmaxf(ramax, __builtin_fabsf(v[w]));
-    }
+    for (int w = 0; w < 32; ++w) ramax = __builtin_fmaxf(ramax, __builtin_fabsf(v[w]));
     const int el = block_exp(ramax);
 #pragma unroll
-    for (int w = 0; w < 32; ++w) lo[w >> 2] |= e4m3_rne(__builtin_ldexpf(v[w], -el)) << (8 * (w & 3));
+    for (int d = 0; d < 8; ++d)
+      lo[d] = e4m3x4(__builtin_ldexpf(v[4 * d], -el), __builtin_ldexpf(v[4 * d + 1], -el),
+                     __builtin_ldexpf(v[4 * d + 2], -el), __builtin_ldexpf(v[4 * d + 3], -el));
     uint8_t* d = qd + (sl * nch + c) * kQData;
     // elements 0-15 and 16-31 of the block are 16 contiguous bytes each
     *reinterpret_cast<uint4*>(d + term_offset(b, 0)) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
@@ -503,25 +512,21 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void ffn_fp4(
           m = __builtin_fmaxf(m, __shfl_xor(m, 16, 64));
           m = __builtin_fmaxf(m, __shfl_xor(m, 32, 64));
           const int eh = block_exp(m);
-          uint32_t hw[2] = {0, 0}, lw[2] = {0, 0};
+          uint32_t hw[2], lw[2];
           float rm = 0.f;
 #pragma unroll
-          for (int half = 0; half < 2; ++half)
+          for (int half = 0; half < 2; ++half) {
+            hw[half] = split_hi(hv[half][0], hv[half][1], hv[half][2], hv[half][3], eh);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const uint32_t ch = e4m3_rne(__builtin_ldexpf(hv[half][v], -eh));
-              hw[half] |= ch << (8 * v);
-              hv[half][v] -= __builtin_ldexpf(e4m3_value(ch), eh);
-              rm = __builtin_fmaxf(rm, __builtin_fabsf(hv[half][v]));
-            }
+            for (int v = 0; v < 4; ++v) rm = __builtin_fmaxf(rm, __builtin_fabsf(hv[half][v]));
+          }
           rm = __builtin_fmaxf(rm, __shfl_xor(rm, 16, 64));
           rm = __builtin_fmaxf(rm, __shfl_xor(rm, 32, 64));
           const int el = block_exp(rm);
 #pragma unroll
           for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              lw[half] |= e4m3_rne(__builtin_ldexpf(hv[half][v], -el)) << (8 * v);
+            lw[half] = e4m3x4(__builtin_ldexpf(hv[half][0], -el), __builtin_ldexpf(hv[half][1], -el),
+                              __builtin_ldexpf(hv[half][2], -el), __builtin_ldexpf(hv[half][3], -el));
           if (t < ntg && n < nvalid) {
             const size_t sl = (uint32_t)slots[t0 + n];
             uint8_t* d = hq_d + (sl * nch_out + cc) * kQData;
