@@ -226,25 +226,37 @@ __global__ __launch_bounds__(256) void quant_x_slots(
 
 // The B operand of one (token group T, MFMA J) step: both terms (8 dwords
 // each) from the LDS data buffer `bd` and the scale dword from the LDS scale
-// buffer `bs`.
+// buffer `bs`. Row n = 16T + r of a buffer stores its granule G at granule
+// G ^ (n & 7) (the copy's bank swizzle); n & 7 = r & 7 for every T, and lane
+// (r, q)'s granules 8J + 2q + {0, 1} (hi term; lo: 16 more) keep J's bit out
+// of the swizzle, so each address is a per-lane offset fixed for the kernel
+// (BOff) plus a compile-time constant the LDS read carries as its immediate.
+struct BOff {
+  uint32_t d0, d1, s;  // granules 2q and 2q + 1 of row r; scale dword q of row r
+};
+__device__ __forceinline__ BOff b_offsets(int r, int q) {
+  BOff o;
+  o.d0 = (uint32_t)(r * kQData + 16 * ((2 * q) ^ (r & 7)));
+  o.d1 = (uint32_t)(r * kQData + 16 * ((2 * q + 1) ^ (r & 7)));
+  o.s = (uint32_t)(r * kQScale + 4 * q);
+  return o;
+}
 struct BFrag {
   v8i h, l;
   int sc;
 };
 template <int T, int J>
-__device__ __forceinline__ BFrag load_b(const unsigned char* bd, const unsigned char* bs, int r,
-                                        int q) {
-  const int n = 16 * T + r;
-  const unsigned char* rowp = bd + n * kQData;
-  const int g0 = 2 * (4 * J + q);  // first granule of this lane's 32 bytes of a term
-  const uint4 h0 = *reinterpret_cast<const uint4*>(rowp + 16 * (g0 ^ (n & 7)));
-  const uint4 h1 = *reinterpret_cast<const uint4*>(rowp + 16 * ((g0 + 1) ^ (n & 7)));
-  const uint4 l0 = *reinterpret_cast<const uint4*>(rowp + 16 * ((16 + g0) ^ (n & 7)));
-  const uint4 l1 = *reinterpret_cast<const uint4*>(rowp + 16 * ((17 + g0) ^ (n & 7)));
+__device__ __forceinline__ BFrag load_b(const unsigned char* bd, const unsigned char* bs,
+                                        const BOff& o) {
+  constexpr uint32_t kRow = 16u * T * kQData + 16u * 8u * J;  // token group T, granule 8J
+  const uint4 h0 = *reinterpret_cast<const uint4*>(bd + (o.d0 + kRow));
+  const uint4 h1 = *reinterpret_cast<const uint4*>(bd + (o.d1 + kRow));
+  const uint4 l0 = *reinterpret_cast<const uint4*>(bd + (o.d0 + (kRow + 256u)));
+  const uint4 l1 = *reinterpret_cast<const uint4*>(bd + (o.d1 + (kRow + 256u)));
   BFrag b;
   b.h = v8i{(int)h0.x, (int)h0.y, (int)h0.z, (int)h0.w, (int)h1.x, (int)h1.y, (int)h1.z, (int)h1.w};
   b.l = v8i{(int)l0.x, (int)l0.y, (int)l0.z, (int)l0.w, (int)l1.x, (int)l1.y, (int)l1.z, (int)l1.w};
-  b.sc = *reinterpret_cast<const int*>(bs + n * kQScale + 4 * q);
+  b.sc = *reinterpret_cast<const int*>(bs + (o.s + 16u * T * kQScale));
   return b;
 }
 
@@ -258,10 +270,12 @@ template <int S, int NT>
 __device__ __forceinline__ void chunk_steps(f32x4 (&acc)[kGroups][kTokGroups],
                                             const AChunk (&a)[kGroups], const int (&sca)[kGroups],
                                             const unsigned char* bd, const unsigned char* bs,
-                                            int r, int q, const BFrag& cur) {
+                                            const BOff& bo, const BFrag& cur) {
   constexpr int T = S / 2, J = S % 2;
+  // the first step's operand reads stay ahead of its scheduling region
+  if constexpr (S == 0) __builtin_amdgcn_sched_barrier(0);
   BFrag nxt;
-  if constexpr (S + 1 < 2 * NT) nxt = load_b<(S + 1) / 2, (S + 1) % 2>(bd, bs, r, q);
+  if constexpr (S + 1 < 2 * NT) nxt = load_b<(S + 1) / 2, (S + 1) % 2>(bd, bs, bo);
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
     const uint4 a4 = J ? a[g].hi : a[g].lo;
@@ -276,8 +290,19 @@ __device__ __forceinline__ void chunk_steps(f32x4 (&acc)[kGroups][kTokGroups],
     acc[g][T] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
         av, cur.l, acc[g][T], kFmtFp4, kFmtFp8, J, sca[g], 2 + J, cur.sc);
   }
+  // The next step's LDS reads go out right after this step's first MFMA, so
+  // the other seven cover their latency. (Left alone, the scheduler issues
+  // them after most of the MFMAs, reusing the current operand's registers,
+  // and the next step waits for them. The wait before the first MFMA counts
+  // all LDS reads, so reads issued before it would be waited for at once.)
+  if constexpr (S + 1 < 2 * NT) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    // 4 x 16 B, and the scale dword when the next step starts a token group
+    __builtin_amdgcn_sched_group_barrier(0x100, S % 2 == 0 ? 4 : 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kGroups - 1, 0);
+  }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (S + 1 < 2 * NT) chunk_steps<S + 1, NT>(acc, a, sca, bd, bs, r, q, nxt);
+  if constexpr (S + 1 < 2 * NT) chunk_steps<S + 1, NT>(acc, a, sca, bd, bs, bo, nxt);
 }
 
 // f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
@@ -324,6 +349,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void ffn_fp4(
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r = lane & 15, q = lane >> 4;
   const uint32_t lw = (uint32_t)r * (uint32_t)wrb, ls = (uint32_t)r * (uint32_t)srb;
+  const BOff bo = b_offsets(r, q);
 
   const int na = *n_active;
   build_tile_prefix<kTok, kWaves>(row_off, na, tpre, wsum);
@@ -460,7 +486,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void ffn_fp4(
             for (int g = 0; g < kGroups; ++g) sca[g] = ok ? (int)ring[slot][g].sc : 0x7f7f;
             const unsigned char* bd = (u & 1) ? buf1 : buf0;
             const unsigned char* bs = (u & 1) ? sbuf1 : sbuf0;
-            chunk_steps<0, NT>(acc, ring[slot], sca, bd, bs, r, q, load_b<0, 0>(bd, bs, r, q));
+            chunk_steps<0, NT>(acc, ring[slot], sca, bd, bs, bo, load_b<0, 0>(bd, bs, bo));
           }
           // The copy of chunk cc + 1 is done once at most the one chunk of
           // weight loads issued after it is outstanding, and this buffer's
