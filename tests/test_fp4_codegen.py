@@ -1,4 +1,4 @@
-"""The FP4 prefill kernel's generated code keeps its weight loads in flight.
+"""The FP4 prefill kernel's generated code keeps its loads in flight.
 
 Each step of `ffn_fp4` issues the next chunk's activation copy (global-to-LDS)
 and weight loads, then runs the current chunk's MFMAs. A wait for every
@@ -7,8 +7,10 @@ make each step wait for the loads it has just issued, so no weight load would
 overlap any arithmetic. The compiler inserts exactly that wait when it is left
 to place the wait for the current chunk's registers (with a global-to-LDS copy
 outstanding it waits for all loads); the kernel therefore waits explicitly at
-the top of the step. This test compiles the kernel for gfx950 (no GPU needed)
-and checks the instruction order in every step of both GEMMs.
+the top of the step. The same holds for the LDS operand reads of each MFMA
+step: they are issued a step ahead, behind the previous step's first MFMA.
+These tests compile the kernel for gfx950 (no GPU needed) and check the
+instruction order in every step of both GEMMs.
 """
 import os
 import re
@@ -85,3 +87,48 @@ def test_no_full_wait_between_weight_loads_and_mfma(asm, gate_up):
             "a wait for every outstanding load sits between the next chunk's weight loads "
             "and this chunk's MFMAs: " + " ".join(seg[:first_mfma + 1]))
     assert checked >= 4, "no steady-state step found in the assembly"
+
+
+def lds_streams(body):
+    """Per segment between barriers: LDS operand reads, MFMAs and LDS waits."""
+    out, cur = [], []
+    for line in body.splitlines():
+        t = line.strip()
+        if t.startswith("s_barrier"):
+            out.append(cur)
+            cur = []
+        elif t.startswith("ds_read_b128"):
+            cur.append("DS")
+        elif t.startswith("v_mfma"):
+            cur.append("MFMA")
+        elif t.startswith("s_waitcnt") and "lgkmcnt" in t:
+            cur.append("LGKM")
+    out.append(cur)
+    return out
+
+
+@pytest.mark.parametrize("gate_up", [True, False], ids=["gate_up", "down"])
+def test_operand_reads_issued_a_step_ahead(asm, gate_up):
+    """Each step's B-operand reads from LDS go out right after the previous
+    step's first MFMA, so that step's other 7 MFMAs run before the wait for
+    them (the wait counts every outstanding LDS read). A schedule that issues
+    them late, after most of the MFMAs, leaves each step waiting for an LDS
+    round trip."""
+    covers = []
+    for seg in lds_streams(kernel_body(asm, gate_up)):
+        if "MFMA" not in seg:
+            continue
+        first_mfma = seg.index("MFMA")
+        for i in range(first_mfma, len(seg)):
+            if seg[i] != "DS":
+                continue
+            n = 0
+            for o in seg[i + 1:]:
+                if o == "LGKM":
+                    break
+                n += o == "MFMA"
+            covers.append(n)
+    assert len(covers) >= 16, "no steady-state operand reads found in the assembly"
+    assert min(covers) >= 7, (
+        "an LDS operand read is followed by fewer than 7 MFMAs before the wait for it: "
+        "min %d over %d reads" % (min(covers), len(covers)))
