@@ -36,17 +36,6 @@ using namespace mx;
 // copied through memcpy, is not promoted to registers and lands in scratch).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// s_waitcnt immediate: at most n vector-memory operations of this wavefront
-// outstanding; LDS and export counters not waited on.
-constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vm_wait_imm(N));
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // ---- down -------------------------------------------------------------------
 //
 // Work item = 16 output rows of one active expert: 16 x I/2 contiguous weight
